@@ -1,0 +1,282 @@
+"""Plain CPU oracle for the head-routed hybrid attention prefill of Elastic Attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
+baseline leg may import this module.  The product path (the HIP library and its
+Python binding) never does, and shares no code, header, table or helper with it.
+
+What is computed, and where the pages define it:
+
+* Boundary pooling of the Key states over the first and last ``pool_len``
+  (= 100) tokens of a sequence, per KV head -> x'_K in R^{H x d'}
+  ("Elastic Attention: Test-time Adaptive Sparsity Ratios for Efficient
+  Transformers", router paragraph on Fig. 3(c) and the boundary-pooling
+  paragraph of the implementation details; "Technical Summary: Elastic
+  Attention", Sec. 2.1).
+* Task MLP then router MLP -> logits z in R^{H x 2} (same passages).
+* Hard routing r_hard = argmax over the two columns, 0 = FA, 1 = SA (router
+  paragraph on Fig. 3(b) and the Gumbel-Softmax paragraph: inference uses
+  hard decisions).
+* Per KV head either full causal attention (FA equation of the preliminaries)
+  or sparse attention over a retained subset of K/V (SA equation); query heads
+  share their group's K/V and mode (GQA footnote of the hybrid-head equation);
+  head outputs are concatenated along features (router paragraph, Fig. 3(b)).
+
+Readings where the pages are silent (the display equations did not survive):
+the softmax scale is 1/sqrt(d); attention is causal; the pooling operator is
+the arithmetic mean over the union of the boundary rows; the MLP activation is
+the exact (erf) GELU; one router is shared by all KV heads of a layer; an
+argmax tie goes to FA; the sparse pattern is static: ``n_sink`` attention-sink
+blocks plus a causal local window of ``w`` blocks of 64 tokens, sized so that
+sinks + window keep ``round(rho * N)`` of the N key blocks.
+
+Every function is written for clarity, not speed: float64 throughout, a
+two-pass softmax over explicitly masked score rows, no tiling, no online
+rescaling, no fusion.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+# ----------------------------------------------------------------------------
+# Router
+# ----------------------------------------------------------------------------
+
+
+def boundary_rows(L: int, pool_len: int) -> np.ndarray:
+    """Sequence-local indices pooled for a sequence of length L: the first
+    ``pool_len`` and the last ``pool_len`` tokens, as a set (a token in both
+    ranges counts once)."""
+    head = np.arange(min(pool_len, L))
+    tail = np.arange(max(0, L - pool_len), L)
+    return np.union1d(head, tail)
+
+
+def boundary_pool(K: np.ndarray, cu_seqlens: np.ndarray, pool_len: int = 100) -> np.ndarray:
+    """x'_K[b, g, :] = mean of K over the boundary rows of sequence b, KV head g.
+
+    K: [T, Hkv, d] (any float dtype).  Returns float64 [B, Hkv, d]; a sequence
+    of length 0 pools to zeros."""
+    B = len(cu_seqlens) - 1
+    T, Hkv, d = K.shape
+    out = np.zeros((B, Hkv, d), dtype=np.float64)
+    for b in range(B):
+        s, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        L = e - s
+        if L <= 0:
+            continue
+        idx = s + boundary_rows(L, pool_len)
+        out[b] = K[idx].astype(np.float64).sum(axis=0) / len(idx)
+    return out
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def linear(x: np.ndarray, W: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """y = x W^T + b with W in [out, in] layout, float64."""
+    return np.asarray(x, np.float64) @ np.asarray(W, np.float64).T + np.asarray(b, np.float64)
+
+
+def router_logits(xp: np.ndarray, w: dict) -> np.ndarray:
+    """Task MLP then router MLP, row-wise over the last axis.
+
+    t = W2 GELU(W1 x' + b1) + b2;  z = W4 GELU(W3 t + b3) + b4."""
+    t = linear(gelu(linear(xp, w["w1"], w["b1"])), w["w2"], w["b2"])
+    return linear(gelu(linear(t, w["w3"], w["b3"])), w["w4"], w["b4"])
+
+
+def route(K: np.ndarray, cu_seqlens: np.ndarray, w: dict, pool_len: int = 100):
+    """Hard FA/SA decision per (sequence, KV head).
+
+    Returns (modes int8 [B, Hkv] with 0 = FA and 1 = SA, logits float64
+    [B, Hkv, 2]).  A tie goes to FA.  An empty sequence gets mode 0 and zero
+    logits."""
+    xp = boundary_pool(K, cu_seqlens, pool_len)
+    z = router_logits(xp, w)
+    lengths = np.diff(np.asarray(cu_seqlens, dtype=np.int64))
+    z[lengths == 0] = 0.0
+    modes = (z[..., 1] > z[..., 0]).astype(np.int8)
+    return modes, z
+
+
+def router_param_count(d: int, task_hidden: int, router_hidden: int) -> int:
+    """Parameters of the two MLPs (weights and biases)."""
+    return (task_hidden * d + task_hidden) + (d * task_hidden + d) + \
+        (router_hidden * d + router_hidden) + (2 * router_hidden + 2)
+
+
+# ----------------------------------------------------------------------------
+# Sparse-attention geometry and visibility
+# ----------------------------------------------------------------------------
+
+
+def sa_geometry(L: int, block: int, n_sink: int, window_blocks: int, keep_fraction: float):
+    """(n_sink, w) for a sequence of length L.
+
+    N = ceil(L / block) key blocks.  With an explicit ``window_blocks`` > 0 the
+    window is that; otherwise the retained block count is
+    keep = max(n_sink + 1, floor(rho * N + 1/2)) with rho the float32 value of
+    ``keep_fraction`` evaluated in double, and w = keep - n_sink."""
+    N = -(-int(L) // int(block))
+    if window_blocks > 0:
+        return int(n_sink), int(window_blocks)
+    rho = float(np.float32(keep_fraction))
+    keep = max(int(n_sink) + 1, int(math.floor(rho * N + 0.5)))
+    return int(n_sink), int(keep - n_sink)
+
+
+def visible(i, j, mode: int, n_sink: int, w: int, block: int):
+    """Whether sequence-local query i may attend to key j.
+
+    FA: causal (j <= i).  SA: causal and (key block is a sink block, or the
+    query's block is fewer than w blocks after the key's block)."""
+    i = np.asarray(i)
+    j = np.asarray(j)
+    causal = j <= i
+    if mode == 0:
+        return causal
+    qb = i // block
+    kb = j // block
+    return causal & ((kb < n_sink) | ((qb - kb) < w))
+
+
+# ----------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------
+
+
+def _attend(q, pos, Kseq, Vseq, mode, n_sink, w, block, scale, return_weights=False):
+    """Two-pass softmax attention of query rows ``q`` [n, d] at sequence
+    positions ``pos`` [n] over one sequence's keys/values [L, d]; float64."""
+    q = np.asarray(q, np.float64)
+    jmax = int(pos.max()) + 1
+    Kc = np.asarray(Kseq[:jmax], np.float64)
+    Vc = np.asarray(Vseq[:jmax], np.float64)
+    s = (q @ Kc.T) * scale
+    mask = visible(pos[:, None], np.arange(jmax)[None, :], mode, n_sink, w, block)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ Vc) / l
+    lse = (m + np.log(l))[:, 0]
+    if return_weights:
+        return o, lse, p / l
+    return o, lse
+
+
+def _scale(d, softmax_scale):
+    return 1.0 / math.sqrt(d) if not softmax_scale else float(np.float32(softmax_scale))
+
+
+def hybrid_attention(Q, K, V, modes, cu_seqlens, *, block=64, n_sink=1, window_blocks=0,
+                     keep_fraction=0.2, softmax_scale=0.0, chunk=512):
+    """Full output of the hybrid layer.
+
+    Q [T, Hq, d], K/V [T, Hkv, d] (values as float32 or float64), modes int8
+    [B, Hkv].  Query head hq reads KV head hq // (Hq / Hkv) and that head's
+    mode.  Returns (O float64 [T, Hq, d], LSE float64 [Hq, T]) with natural-log
+    LSE = m + ln(sum exp(s - m))."""
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = _scale(d, softmax_scale)
+    O = np.zeros((T, Hq, d), dtype=np.float64)
+    LSE = np.zeros((Hq, T), dtype=np.float64)
+    for b in range(len(cu_seqlens) - 1):
+        s0, e0 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        L = e0 - s0
+        if L <= 0:
+            continue
+        ns, w = sa_geometry(L, block, n_sink, window_blocks, keep_fraction)
+        for hq in range(Hq):
+            g = hq // G
+            mode = int(modes[b, g])
+            for r0 in range(0, L, chunk):
+                r1 = min(L, r0 + chunk)
+                pos = np.arange(r0, r1)
+                o, lse = _attend(Q[s0 + r0:s0 + r1, hq], pos, K[s0:e0, g], V[s0:e0, g], mode,
+                                 ns, w, block, scale)
+                O[s0 + r0:s0 + r1, hq] = o
+                LSE[hq, s0 + r0:s0 + r1] = lse
+    return O, LSE
+
+
+def hybrid_attention_rows(Q, K, V, modes, cu_seqlens, tokens, heads, *, block=64, n_sink=1,
+                          window_blocks=0, keep_fraction=0.2, softmax_scale=0.0):
+    """The same output at selected global token indices and query heads only.
+
+    Returns (O float64 [len(tokens), len(heads), d], LSE float64
+    [len(tokens), len(heads)])."""
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = _scale(d, softmax_scale)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    seg = np.searchsorted(np.asarray(cu_seqlens, np.int64), tokens, side="right") - 1
+    O = np.zeros((len(tokens), len(heads), d), dtype=np.float64)
+    LSE = np.zeros((len(tokens), len(heads)), dtype=np.float64)
+    for b in np.unique(seg):
+        s0, e0 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        L = e0 - s0
+        ns, w = sa_geometry(L, block, n_sink, window_blocks, keep_fraction)
+        sel = np.nonzero(seg == b)[0]
+        pos = tokens[sel] - s0
+        for hi, hq in enumerate(heads):
+            g = hq // G
+            o, lse = _attend(Q[tokens[sel], hq], pos, K[s0:e0, g], V[s0:e0, g], int(modes[b, g]),
+                             ns, w, block, scale)
+            O[sel, hi] = o
+            LSE[sel, hi] = lse
+    return O, LSE
+
+
+def attention_weights(Q, K, modes, L, hq, *, G, block=64, n_sink=1, window_blocks=0,
+                      keep_fraction=0.2, softmax_scale=0.0):
+    """The L x L row-stochastic weight matrix of query head hq for a single
+    sequence of length L starting at token 0 (small cases only)."""
+    d = Q.shape[2]
+    g = hq // G
+    ns, w = sa_geometry(L, block, n_sink, window_blocks, keep_fraction)
+    Vdummy = np.zeros((L, 1))
+    _, _, P = _attend(Q[:L, hq], np.arange(L), K[:L, g], Vdummy, int(modes[0, g]), ns, w, block,
+                      _scale(d, softmax_scale), return_weights=True)
+    return P
+
+
+# ----------------------------------------------------------------------------
+# Effective FLOPs
+# ----------------------------------------------------------------------------
+
+
+def effective_flops(modes, cu_seqlens, Hq, Hkv, d, *, block=64, n_sink=1, window_blocks=0,
+                    keep_fraction=0.2) -> int:
+    """4 d * sum over query heads and visible (query block, key block) pairs of
+    rows(qb) * cols(kb); a pair is visible when any (i, j) in it is visible, and
+    a partly visible (diagonal or window-edge) pair counts in full."""
+    G = Hq // Hkv
+    total = 0
+    for b in range(len(cu_seqlens) - 1):
+        L = int(cu_seqlens[b + 1]) - int(cu_seqlens[b])
+        if L <= 0:
+            continue
+        ns, w = sa_geometry(L, block, n_sink, window_blocks, keep_fraction)
+        N = -(-L // block)
+        size = np.minimum(block, L - block * np.arange(N))
+        for g in range(Hkv):
+            mode = int(modes[b, g])
+            acc = 0
+            for qb in range(N):
+                kb = np.arange(qb + 1)
+                # block-level visibility: the last row of the query block sees key
+                # block kb's first key iff some pair of the two blocks is visible
+                ok = visible(qb * block + size[qb] - 1, kb * block, mode, ns, w, block)
+                acc += int(size[qb]) * int(size[kb][ok].sum())
+            total += G * acc
+    return 4 * d * total
