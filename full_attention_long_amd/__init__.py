@@ -1,0 +1,16 @@
+"""MI355X-native head-routed hybrid attention prefill (Elastic Attention's inference path).
+
+The compute lives in libea.so (HIP for gfx950, C ABI in include/ea.h); this
+package holds the ctypes binding and the host-side bookkeeping used to report
+throughput.
+"""
+from .binding import (  # noqa: F401
+    EAError,
+    ea_abi_version,
+    ea_hybrid_prefill,
+    ea_hybrid_prefill_workspace_size,
+    ea_last_error,
+    ea_route,
+    header_functions,
+    lib,
+)

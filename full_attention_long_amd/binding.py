@@ -1,0 +1,169 @@
+"""ctypes binding of libea (argument marshalling only).
+
+Every step of the routed hybrid prefill runs in the library's HIP kernels;
+this module only converts torch device tensors to pointers and sizes, provides
+outputs and workspace as torch allocations, and turns error codes into
+exceptions.  It has no CPU fallback: without the built library it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libea.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "ea.h")
+
+EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_HIP = 0, -1, -2, -3, -4
+EA_F32, EA_BF16 = 0, 1
+
+
+class EAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libea status {status}: {message}")
+        self.status = status
+
+
+class RouterDesc(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32), ("task_hidden", ctypes.c_int32),
+        ("router_hidden", ctypes.c_int32), ("pool_len", ctypes.c_int32),
+        ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+        ("b2", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("b3", ctypes.c_void_p),
+        ("w4", ctypes.c_void_p), ("b4", ctypes.c_void_p),
+    ]
+
+
+class SparsityParams(ctypes.Structure):
+    _fields_ = [
+        ("block", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
+        ("window_blocks", ctypes.c_int32), ("keep_fraction", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libea.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m full_attention_long_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.ea_abi_version.restype = i32
+    L.ea_abi_version.argtypes = []
+    L.ea_last_error.restype = ctypes.c_char_p
+    L.ea_last_error.argtypes = []
+    L.ea_route.restype = i32
+    L.ea_route.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(RouterDesc), vp, vp, vp]
+    L.ea_hybrid_prefill_workspace_size.restype = sz
+    L.ea_hybrid_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.ea_hybrid_prefill.restype = i32
+    L.ea_hybrid_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                    ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/ea.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ea_status|size_t|int32_t|const char\*)\s+(ea_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def _check(status: int):
+    if status != EA_OK:
+        raise EAError(status, lib().ea_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return EA_BF16
+    if t.dtype == torch.float32:
+        return EA_F32
+    raise EAError(EA_ERR_UNSUPPORTED, f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name):
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise EAError(EA_ERR_INVALID_ARG, f"{name} must be a contiguous device tensor")
+    return t
+
+
+def ea_abi_version() -> int:
+    return int(lib().ea_abi_version())
+
+
+def ea_last_error() -> str:
+    return lib().ea_last_error().decode()
+
+
+def ea_route(K, cu_seqlens, weights: dict, *, pool_len: int = 100, modes=None, logits=None,
+             with_logits: bool = True, stream=None):
+    """Hard FA/SA modes (int8 [B, Hkv]) and logits (float32 [B, Hkv, 2]) from K [T, Hkv, d]."""
+    import torch
+    _dev(K, "K")
+    _dev(cu_seqlens, "cu_seqlens")
+    B = cu_seqlens.numel() - 1
+    Hkv, d = K.shape[1], K.shape[2]
+    w = {k: _dev(weights[k], k) for k in ["w1", "b1", "w2", "b2", "w3", "b3", "w4", "b4"]}
+    desc = RouterDesc(d, w["w1"].shape[0], w["w3"].shape[0], pool_len,
+                      *[w[k].data_ptr() for k in ["w1", "b1", "w2", "b2", "w3", "b3", "w4", "b4"]])
+    if modes is None:
+        modes = torch.empty((B, Hkv), dtype=torch.int8, device=K.device)
+    if logits is None and with_logits:
+        logits = torch.empty((B, Hkv, 2), dtype=torch.float32, device=K.device)
+    _check(lib().ea_route(_ptr(K), _dtype_code(K), _ptr(cu_seqlens), B, Hkv, ctypes.byref(desc),
+                          _ptr(modes), _ptr(logits), _stream(stream)))
+    return modes, logits
+
+
+def ea_hybrid_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype_code):
+    return int(lib().ea_hybrid_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv,
+                                                      head_dim, dtype_code))
+
+
+def ea_hybrid_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: int = 1,
+                      window_blocks: int = 0, keep_fraction: float = 0.2,
+                      softmax_scale: float = 0.0, block: int = 64, out=None, lse=None,
+                      with_lse: bool = True, workspace=None, stream=None):
+    """O [T, Hq, d] (and LSE float32 [Hq, T]) of the fused hybrid attention forward."""
+    import torch
+    for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (modes, "modes"), (cu_seqlens, "cu_seqlens")]:
+        _dev(t, n)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    B = cu_seqlens.numel() - 1
+    code = _dtype_code(Q)
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is None and with_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=Q.device)
+    need = ea_hybrid_prefill_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    _check(lib().ea_hybrid_prefill(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes), _ptr(cu_seqlens),
+                                   B, T, max_seqlen, Hq, Hkv, d, ctypes.byref(sp), _ptr(out),
+                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse

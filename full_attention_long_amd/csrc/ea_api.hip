@@ -1,0 +1,142 @@
+// C ABI of libea: argument validation and stream-ordered launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ea_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ea_status fail(ea_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ea_status ok() {
+  g_err.clear();
+  return EA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates the sizes shared by the workspace query and the prefill call.
+ea_status check_shape(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                      int32_t d, ea_dtype dtype, ea::Shape* out) {
+  if (B < 1) return fail(EA_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+  if (T < 0 || T >= (int64_t(1) << 31))
+    return fail(EA_ERR_INVALID_ARG, "total_tokens must be in [0, 2^31) (got %lld)", (long long)T);
+  if (T > 0 && (max_seqlen < 1 || max_seqlen > T))
+    return fail(EA_ERR_INVALID_ARG, "max_seqlen must be in [1, total_tokens] (got %d)", max_seqlen);
+  if (Hq < 1 || Hkv < 1) return fail(EA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
+  if (Hq % Hkv != 0) return fail(EA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  const int32_t G = Hq / Hkv;
+  if (G > ea::kTileRows)
+    return fail(EA_ERR_UNSUPPORTED, "Hq / Hkv must be <= %d (got %d)", ea::kTileRows, G);
+  if (d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d);
+  if (dtype != EA_F32 && dtype != EA_BF16) return fail(EA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  out->B = B;
+  out->T = T;
+  out->max_seqlen = T > 0 ? max_seqlen : 1;
+  out->Hq = Hq;
+  out->Hkv = Hkv;
+  out->d = d;
+  out->G = G;
+  out->BMq = ea::kTileRows / G;
+  out->elem_bytes = dtype == EA_BF16 ? 2 : 4;
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ea_abi_version(void) { return EA_ABI_VERSION; }
+
+const char* ea_last_error(void) { return g_err.c_str(); }
+
+ea_status ea_route(const void* K, ea_dtype dtype, const int32_t* cu_seqlens, int32_t B,
+                   int32_t Hkv, const ea_router_desc* r, int8_t* modes, float* logits,
+                   void* stream) {
+  if (!K || !cu_seqlens || !r || !modes) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (dtype != EA_F32 && dtype != EA_BF16) return fail(EA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (B < 1 || Hkv < 1) return fail(EA_ERR_INVALID_ARG, "B and Hkv must be >= 1");
+  if ((int64_t)B * Hkv >= (int64_t(1) << 31)) return fail(EA_ERR_INVALID_ARG, "B * Hkv too large");
+  if (r->head_dim < 1 || r->head_dim > 256)
+    return fail(EA_ERR_UNSUPPORTED, "router head_dim must be in [1, 256] (got %d)", r->head_dim);
+  if (r->task_hidden < 1 || r->task_hidden > 4096)
+    return fail(EA_ERR_UNSUPPORTED, "task_hidden must be in [1, 4096] (got %d)", r->task_hidden);
+  if (r->router_hidden < 1 || r->router_hidden > 1024)
+    return fail(EA_ERR_UNSUPPORTED, "router_hidden must be in [1, 1024] (got %d)", r->router_hidden);
+  if (r->pool_len < 1) return fail(EA_ERR_INVALID_ARG, "pool_len must be >= 1 (got %d)", r->pool_len);
+  if (!r->w1 || !r->b1 || !r->w2 || !r->b2 || !r->w3 || !r->b3 || !r->w4 || !r->b4)
+    return fail(EA_ERR_INVALID_ARG, "null router weight pointer");
+  hipError_t e = ea::launch_route(K, dtype == EA_BF16, cu_seqlens, B, Hkv, *r, modes, logits,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "route launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                        int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                        ea_dtype dtype) {
+  ea::Shape s;
+  if (check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s) != EA_OK) return 0;
+  g_err.clear();
+  return ea::plan_workspace(s).total;
+}
+
+ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                            const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                            int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                            int32_t head_dim, const ea_sparsity_params* p, void* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea_status st = check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s);
+  if (st != EA_OK) return st;
+  if (!p) return fail(EA_ERR_INVALID_ARG, "null sparsity params");
+  if (p->block != ea::kBlock)
+    return fail(EA_ERR_UNSUPPORTED, "sparsity block must be %d (got %d)", ea::kBlock, p->block);
+  if (p->n_sink_blocks < 0) return fail(EA_ERR_INVALID_ARG, "n_sink_blocks must be >= 0");
+  if (p->window_blocks < 0) return fail(EA_ERR_INVALID_ARG, "window_blocks must be >= 0");
+  if (p->window_blocks == 0 && !(p->keep_fraction > 0.f && p->keep_fraction <= 1.f))
+    return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1] (got %g)", (double)p->keep_fraction);
+  if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+    return fail(EA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!Q || !K || !V || !modes || !cu_seqlens || !O)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(EA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+  const ea::Workspace ws = ea::plan_workspace(s);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (total_tokens == 0) return ok();
+
+  ea::Geometry g;
+  g.n_sink = p->n_sink_blocks;
+  g.window_blocks = p->window_blocks;
+  g.keep_fraction = p->keep_fraction;
+  g.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  g.scale_log2 = g.scale * 1.44269504088896340736f;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e == hipSuccess) e = ea::launch_transpose_v(s, V, cu_seqlens, ws, base, hs);
+  if (e == hipSuccess) e = ea::launch_attention(s, g, Q, K, modes, cu_seqlens, O, lse, ws, base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

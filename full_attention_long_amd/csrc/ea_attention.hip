@@ -1,0 +1,354 @@
+// Fused hybrid GQA attention forward for gfx950: every work item, FA or SA, in
+// one launch.
+//
+// Pages: FA and SA equations of the preliminaries and the hybrid-head output
+// equation (with its GQA footnote) in "Elastic Attention: Test-time Adaptive
+// Sparsity Ratios for Efficient Transformers"; the single fused pass over
+// mixed-mode heads is "Technical Summary: Elastic Attention", Sec. 2.3.  The
+// sparse pattern (sink blocks + causal local window, 64-token blocks) and the
+// softmax scale 1/sqrt(d) are the readings stated in ea.h.
+//
+// Work item = query tile of one KV-head group: 128 rows = G heads x BMq
+// positions, one wave per 32 rows.  Each wave computes the transposed score
+// tile S^T = K Q^T (keys x queries) with 32x32 MFMAs so that every lane owns
+// one query row: the row max needs one cross-half exchange per key block and
+// the row sum none until the epilogue.  Probabilities P^T stay in registers in
+// the MFMA result layout and feed O^T += V^T P^T directly; V^T comes from a
+// transposed copy of V whose key order matches that layout.  K and V^T blocks
+// of 64 keys are double-buffered through LDS: the next block's coalesced
+// 16-byte global loads are issued before the current block's MFMAs and land
+// in the other buffer after them, one barrier per block.
+//
+// Online softmax in base 2 (scale * log2 e folded into one FMA per score) with
+// a lazy rescale: the running max only moves, and O and l are only rescaled,
+// when a row's block max exceeds it by more than 8 (probabilities stay <= 2^8,
+// the ratio O / l is unchanged).
+#include "ea_internal.h"
+
+#include <type_traits>
+
+namespace ea {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kMinusBig = -1.0e30f;      // finite "minus infinity" for the running max
+
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* Vt;
+  void* O;
+  float* lse;
+  const int8_t* modes;
+  const int32_t* cu;
+  const int32_t* seq_w;
+  const int32_t* vblk_prefix;
+  const Item* items;
+  const int32_t* meta;
+  int64_t T;
+  int64_t tpad;
+  int32_t Hq, Hkv, G, BMq, n_sink;
+  float scale_log2;
+};
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
+  f32x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = s[base + e];
+  return __builtin_convertvector(v, bf16x8);
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256, BF16 ? 2 : 1) void attention_kernel(AttnArgs a) {
+  using E = std::conditional_t<BF16, uint16_t, float>;
+  constexpr int CH = 16 / sizeof(E);       // elements per 16-byte chunk
+  constexpr int KROW = D + CH;             // padded LDS row of K (elements)
+  constexpr int VROW = kBlock + CH;        // padded LDS row of V^T (elements)
+  constexpr int NLD = kBlock * D / CH / 256;  // 16-byte chunks per thread per block
+  constexpr int DT = D / 32;               // 32-wide dim tiles of O^T
+  static_assert(NLD * 256 * CH == kBlock * D, "tile must split evenly over 256 threads");
+
+  __shared__ __attribute__((aligned(16))) E Ks[2][kBlock * KROW];
+  __shared__ __attribute__((aligned(16))) E Vs[2][D * VROW];
+
+  if (static_cast<int32_t>(blockIdx.x) >= a.meta[kMetaItems]) return;
+  const Item it = a.items[blockIdx.x];
+  const int b = it.b, kvh = it.kvh;
+  const int tok0 = a.cu[b];
+  const int L = a.cu[b + 1] - tok0;
+  const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + kvh] != 0 ? 1 : 0;
+  const int ns = a.n_sink;
+  const int w = a.seq_w[b];
+  const int p0 = it.qt * a.BMq;
+  const int p1 = min(p0 + a.BMq, L) - 1;
+  const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
+
+  // Visible key blocks: FA [0, qb1]; SA sinks [0, r1_end) then window [r2_beg, qb1].
+  int r1_end = 0, r2_beg = 0;
+  if (mode) {
+    const int ws = max(0, qb0 - w + 1);
+    r1_end = min(ns, ws);
+    r2_beg = ws;
+  }
+  const int nblk = r1_end + (qb1 + 1 - r2_beg);
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, h = lane / 32, lq = lane % 32;
+  const int row = wave * 32 + lq;
+  const int hh = row / a.BMq;
+  const int pos = p0 + row % a.BMq;
+  const bool rvalid = hh < a.G && pos < L;
+  const int hq = kvh * a.G + hh;
+  const int qblk = pos / kBlock;
+
+  const E* Qp = static_cast<const E*>(a.Q);
+  const E* Kp = static_cast<const E*>(a.K);
+  const E* Vtp = static_cast<const E*>(a.Vt);
+  const int64_t vcol0 = static_cast<int64_t>(a.vblk_prefix[b]) * kBlock;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
+  using QFrag = std::conditional_t<BF16, bf16x8, f32x4>;
+  constexpr int NQ = BF16 ? D / 16 : D / 8;
+  QFrag qf[NQ];
+  {
+    const E* qrow = Qp + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      if (rvalid) {
+        qf[u] = *reinterpret_cast<const QFrag*>(qrow + (BF16 ? 16 * u : 8 * u) + 4 * (BF16 ? 2 : 1) * h);
+      } else {
+        qf[u] = QFrag{};
+      }
+    }
+  }
+
+  // ---- global -> register -> LDS staging of one key block ----
+  u32x4 kreg[NLD], vreg[NLD];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int c = n * 256 + tid;
+      const int krow = c / (D / CH), kcol = (c % (D / CH)) * CH;
+      const int key = kb * kBlock + krow;
+      if (key < L) {
+        kreg[n] = *reinterpret_cast<const u32x4*>(
+            Kp + (static_cast<int64_t>(tok0 + key) * a.Hkv + kvh) * D + kcol);
+      } else {
+        kreg[n] = u32x4{0, 0, 0, 0};
+      }
+      const int vrow = c / (kBlock / CH), vcol = (c % (kBlock / CH)) * CH;
+      vreg[n] = *reinterpret_cast<const u32x4*>(
+          Vtp + (static_cast<int64_t>(kvh) * D + vrow) * a.tpad + vcol0 + kb * kBlock + vcol);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int c = n * 256 + tid;
+      const int krow = c / (D / CH), kcol = (c % (D / CH)) * CH;
+      *reinterpret_cast<u32x4*>(&Ks[buf][krow * KROW + kcol]) = kreg[n];
+      const int vrow = c / (kBlock / CH), vcol = (c % (kBlock / CH)) * CH;
+      *reinterpret_cast<u32x4*>(&Vs[buf][vrow * VROW + vcol]) = vreg[n];
+    }
+  };
+  auto kb_of = [&](int n) { return n < r1_end ? n : r2_beg + (n - r1_end); };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+  float m_run = kMinusBig, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  gload(kb_of(0));
+  lstore(0);
+  __syncthreads();
+
+  for (int n = 0; n < nblk; ++n) {
+    const int kb = kb_of(n);
+    const int buf = n & 1;
+    if (n + 1 < nblk) gload(kb_of(n + 1));
+
+    // ---- S^T tiles: keys [0,32) and [32,64) of the block x this wave's 32 queries ----
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    const E* k0 = &Ks[buf][lq * KROW];
+    const E* k1 = &Ks[buf][(32 + lq) * KROW];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k0 + 16 * u + 8 * h);
+        const bf16x8 kb2 = *reinterpret_cast<const bf16x8*>(k1 + 16 * u + 8 * h);
+        s0 = mfma_bf16(ka, qf[u], s0);
+        s1 = mfma_bf16(kb2, qf[u], s1);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < D / 8; ++g) {
+        const f32x4 ka = *reinterpret_cast<const f32x4*>(k0 + 8 * g + 4 * h);
+        const f32x4 kb2 = *reinterpret_cast<const f32x4*>(k1 + 8 * g + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s0 = mfma_f32(ka[e], qf[g][e], s0);
+          s1 = mfma_f32(kb2[e], qf[g][e], s1);
+        }
+      }
+    }
+
+    // ---- mask the diagonal and window-edge blocks (element (i) is key 8(i/4)+4h+(i%4)) ----
+    const bool full = (kb * kBlock + kBlock - 1 <= p0) && (mode == 0 || kb < ns || qb1 - kb < w);
+    if (!full) {
+      const bool blk_ok = mode == 0 || kb < ns || qblk - kb < w;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
+        if (!(blk_ok && j <= pos)) s0[i] = -INFINITY;
+        if (!(blk_ok && j + 32 <= pos)) s1[i] = -INFINITY;
+      }
+    }
+
+    // ---- online softmax (base 2, lazy rescale) ----
+    float mx = s0[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mc = mx * c;
+    if (__ballot(mc > m_run + kRescaleThreshold)) {
+      const float mn = fmaxf(m_run, mc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    }
+    const float nm = -m_run;
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, nm));
+      s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, nm));
+      ls += s0[i] + s1[i];
+    }
+    l_run += ls;
+
+    // ---- O^T += V^T P^T ----
+    if constexpr (BF16) {
+      bf16x8 pb[4];
+      pb[0] = to_bf16x8(s0, 0);
+      pb[1] = to_bf16x8(s0, 8);
+      pb[2] = to_bf16x8(s1, 0);
+      pb[3] = to_bf16x8(s1, 8);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const E* vrow = &Vs[buf][(32 * t + lq) * VROW + 8 * h];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * u);
+          o[t] = mfma_bf16(vf, pb[u], o[t]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const E* vrow = &Vs[buf][(32 * t + lq) * VROW + 8 * h];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 va = *reinterpret_cast<const f32x4*>(vrow + 16 * u);
+          const f32x4 vb = *reinterpret_cast<const f32x4*>(vrow + 16 * u + 4);
+          const f32x16& p = (u < 2) ? s0 : s1;
+          const int base = 8 * (u & 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[t] = mfma_f32(va[e], p[base + e], o[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[t] = mfma_f32(vb[e], p[base + 4 + e], o[t]);
+        }
+      }
+    }
+
+    if (n + 1 < nblk) lstore((n + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, written in place in [T, Hq, D]; LSE ----
+  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / lt;
+  if (rvalid) {
+    E* orow = static_cast<E*>(a.O) + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = 32 * t + 8 * q + 4 * h;
+        if constexpr (BF16) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[t][4 * q + e] * inv;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<bf16x4*>(orow + dim) = __builtin_convertvector(v, bf16x4);
+        } else {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[t][4 * q + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + dim) = v;
+        }
+      }
+    }
+    if (h == 0 && a.lse) a.lse[static_cast<int64_t>(hq) * a.T + tok0 + pos] = (m_run + __log2f(lt)) * kLn2;
+  }
+}
+
+template <bool BF16, int D>
+void launch(const AttnArgs& args, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((attention_kernel<BF16, D>), dim3(grid), dim3(256), 0, st, args);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
+                            const int8_t* modes, const int32_t* cu, void* O, float* lse,
+                            const Workspace& ws, char* base, hipStream_t st) {
+  AttnArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.Vt = base + ws.vt;
+  a.O = O;
+  a.lse = lse;
+  a.modes = modes;
+  a.cu = cu;
+  a.seq_w = reinterpret_cast<const int32_t*>(base + ws.seq_w);
+  a.vblk_prefix = reinterpret_cast<const int32_t*>(base + ws.vblk_prefix);
+  a.items = reinterpret_cast<const Item*>(base + ws.items);
+  a.meta = reinterpret_cast<const int32_t*>(base + ws.meta);
+  a.T = s.T;
+  a.tpad = ws.tpad;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.BMq = s.BMq;
+  a.n_sink = g.n_sink;
+  a.scale_log2 = g.scale_log2;
+  const unsigned grid = static_cast<unsigned>(ws.max_items);
+  const bool bf16 = s.elem_bytes == 2;
+  if (bf16 && s.d == 128) launch<true, 128>(a, grid, st);
+  else if (bf16 && s.d == 64) launch<true, 64>(a, grid, st);
+  else if (!bf16 && s.d == 128) launch<false, 128>(a, grid, st);
+  else launch<false, 64>(a, grid, st);
+  return hipGetLastError();
+}
+
+}  // namespace ea

@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP translation units of libea.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ea.h"
+
+namespace ea {
+
+// Query rows per attention work item: G query heads x (128 / G) positions.
+constexpr int kTileRows = 128;
+// Key/value block of the sparse pattern and of the attention inner loop.
+constexpr int kBlock = 64;
+
+// One attention work item: a query tile of one KV-head group of one sequence.
+struct Item {
+  int32_t b;     // sequence
+  int32_t kvh;   // KV head
+  int32_t qt;    // query tile: positions [qt * BMq, qt * BMq + BMq)
+  int32_t cost;  // visible key blocks (scheduling key)
+};
+
+// Slots of the small int32 header at the start of the workspace.
+enum Meta : int {
+  kMetaItems = 0,       // number of work items
+  kMetaTiles = 1,       // sum over sequences of ceil(L_b / BMq)
+  kMetaVBlocks = 2,     // sum over sequences of ceil(L_b / 64)
+  kMetaSlots = 64
+};
+
+// Byte layout of the workspace, a pure function of the host-visible sizes.
+struct Workspace {
+  size_t meta, tile_prefix, vblk_prefix, seq_w, hist, cursor, items_raw, items, vt, total;
+  int64_t max_items;   // bound on work items
+  int64_t tpad;        // row stride (tokens) of the transposed V copy
+  int32_t nbins;       // cost histogram bins
+};
+
+struct Shape {
+  int32_t B;
+  int64_t T;
+  int32_t max_seqlen, Hq, Hkv, d, G, BMq;
+  int32_t elem_bytes;
+};
+
+Workspace plan_workspace(const Shape& s);
+
+struct Geometry {
+  int32_t n_sink;
+  int32_t window_blocks;   // 0: per sequence from keep_fraction
+  float keep_fraction;
+  float scale_log2;        // softmax scale * log2(e)
+  float scale;             // softmax scale
+};
+
+// Launchers (stream-ordered, no synchronisation).  Return hipSuccess or the
+// launch error.
+hipError_t launch_route(const void* K, bool bf16, const int32_t* cu, int32_t B, int32_t Hkv,
+                        const ea_router_desc& r, int8_t* modes, float* logits, hipStream_t st);
+
+hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,
+                           const int32_t* cu, const Workspace& ws, char* base, hipStream_t st);
+
+hipError_t launch_transpose_v(const Shape& s, const void* V, const int32_t* cu,
+                              const Workspace& ws, char* base, hipStream_t st);
+
+hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
+                            const int8_t* modes, const int32_t* cu, void* O, float* lse,
+                            const Workspace& ws, char* base, hipStream_t st);
+
+}  // namespace ea

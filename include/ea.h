@@ -1,0 +1,162 @@
+/*
+ * ea.h - C ABI of the MI355X (gfx950) head-routed hybrid attention prefill.
+ *
+ * The method is Elastic Attention's inference path ("Elastic Attention:
+ * Test-time Adaptive Sparsity Ratios for Efficient Transformers"; summarised
+ * in "Technical Summary: Elastic Attention"):
+ *
+ *   1. an attention router pools the Key states of each KV head over the first
+ *      and last 100 tokens, runs a task MLP and a router MLP to logits
+ *      z in R^{H x 2}, and takes the argmax as a hard per-head decision,
+ *      0 = full attention (FA), 1 = sparse attention (SA)
+ *      (paper body: router paragraphs on Fig. 3(b) and Fig. 3(c), boundary
+ *      pooling in the implementation details; summary Sec. 2.1);
+ *   2. one fused GQA attention forward then serves every head in a single
+ *      pass, FA heads attending causally to all keys and SA heads to a
+ *      retained subset of K/V, with the head outputs concatenated along the
+ *      feature axis (paper body: FA and SA equations of the preliminaries,
+ *      hybrid-head output equation and its GQA footnote; summary Sec. 2.3).
+ *
+ * The sparse subset is static: n_sink attention-sink blocks plus a causal
+ * local window of w key blocks, in blocks of 64 tokens, with
+ * w = max(n_sink + 1, floor(rho * N + 1/2)) - n_sink for N = ceil(L / 64)
+ * key blocks (rho = keep_fraction) unless window_blocks > 0 gives w directly.
+ * Query i (sequence-local) sees key j iff j <= i and (mode == FA or
+ * j / 64 < n_sink or i / 64 - j / 64 < w).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory and keeps no state between calls.
+ *  - Tensors are dense and row-major with the last axis innermost; sequences
+ *    are packed back to back ("varlen"), delimited by cu_seqlens (int32,
+ *    [B + 1], cu_seqlens[0] = 0, non-decreasing).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise the host.
+ *  - Host-checkable errors return a negative status before anything is
+ *    launched; ea_last_error() then returns a message (thread-local).  A
+ *    failed launch returns EA_ERR_HIP.  Device contents (cu_seqlens values,
+ *    mode values) are preconditions and are not read by the host.
+ */
+#ifndef EA_H
+#define EA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EA_ABI_VERSION 1
+
+typedef enum {
+  EA_OK = 0,
+  EA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad value */
+  EA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, dtype, block size */
+  EA_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+  EA_ERR_HIP = -4          /* a HIP launch failed; message has the HIP error */
+} ea_status;
+
+typedef enum {
+  EA_F32 = 0,  /* float32 */
+  EA_BF16 = 1  /* bfloat16 (arithmetic: bf16 MFMA operands, fp32 accumulate) */
+} ea_dtype;
+
+/* Router parameters: float32 device arrays in nn.Linear layout [out, in].
+ *   task MLP:   t = W2 GELU(W1 x' + b1) + b2      W1 [task_hidden, head_dim],
+ *                                                  W2 [head_dim, task_hidden]
+ *   router MLP: z = W4 GELU(W3 t + b3) + b4       W3 [router_hidden, head_dim],
+ *                                                  W4 [2, router_hidden]
+ * GELU is the exact erf form.  One router is shared by all KV heads.
+ * Limits: 1 <= head_dim <= 256, 1 <= task_hidden <= 4096,
+ * 1 <= router_hidden <= 1024, pool_len >= 1 (the pages use 100). */
+typedef struct {
+  int32_t head_dim;
+  int32_t task_hidden;
+  int32_t router_hidden;
+  int32_t pool_len;
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+  const float* w3;
+  const float* b3;
+  const float* w4;
+  const float* b4;
+} ea_router_desc;
+
+/* Sparse-attention geometry and softmax scale.
+ *   block          must be 64
+ *   n_sink_blocks  >= 0 attention-sink blocks kept by SA heads
+ *   window_blocks  > 0: local window of that many blocks; 0: derive it from
+ *                  keep_fraction per sequence (formula above, evaluated in
+ *                  double on the float32 value)
+ *   keep_fraction  in (0, 1]; read only when window_blocks == 0
+ *   softmax_scale  > 0, or 0 for 1/sqrt(head_dim) */
+typedef struct {
+  int32_t block;
+  int32_t n_sink_blocks;
+  int32_t window_blocks;
+  float keep_fraction;
+  float softmax_scale;
+} ea_sparsity_params;
+
+/* ABI version of the loaded library (EA_ABI_VERSION it was built with). */
+int32_t ea_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ea_last_error(void);
+
+/* ea_route - hard FA/SA decision per (sequence, KV head).
+ *
+ *   K           [T, Hkv, head_dim] of `dtype` (16-byte aligned); only the
+ *               boundary rows of each sequence are read
+ *   cu_seqlens  int32 [B + 1]
+ *   router      parameters (struct on the host, arrays on the device)
+ *   modes       out int8 [B, Hkv]: 0 = FA, 1 = SA; argmax of z with ties to FA
+ *   logits      out float32 [B, Hkv, 2], or NULL
+ *
+ * Pooling is the mean over the union of a sequence's first and last pool_len
+ * rows (a row in both counts once), accumulated in float32.  An empty
+ * sequence gets mode 0 and logits (0, 0). */
+ea_status ea_route(const void* K, ea_dtype dtype, const int32_t* cu_seqlens, int32_t B,
+                   int32_t Hkv, const ea_router_desc* router, int8_t* modes, float* logits,
+                   void* stream);
+
+/* Bytes of device workspace ea_hybrid_prefill needs for these sizes (0 if the
+ * sizes are invalid).  The workspace holds the per-launch work list and a
+ * transposed copy of V; its contents need not be initialised. */
+size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                        int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                        ea_dtype dtype);
+
+/* ea_hybrid_prefill - fused hybrid GQA attention forward over all heads.
+ *
+ *   Q           [T, Hq, head_dim]  of `dtype` (16-byte aligned)
+ *   K, V        [T, Hkv, head_dim] of `dtype` (16-byte aligned)
+ *   modes       int8 [B, Hkv], values 0 (FA) or 1 (SA); query head hq uses
+ *               KV head hq / (Hq / Hkv) and its mode
+ *   cu_seqlens  int32 [B + 1]; total_tokens = cu_seqlens[B] = T < 2^31
+ *   max_seqlen  >= every sequence length (>= 1 when T > 0)
+ *   params      sparse geometry and scale (host struct)
+ *   O           out [T, Hq, head_dim] of `dtype`, written in place: no
+ *               per-mode gather or scatter
+ *   lse         out float32 [Hq, T] natural-log sum of exp of the scaled
+ *               visible scores, or NULL
+ *   workspace   device buffer of >= ea_hybrid_prefill_workspace_size() bytes
+ *               (256-byte aligned); not shared between concurrent calls
+ *
+ * head_dim must be 64 or 128; Hq must be a multiple of Hkv with
+ * Hq / Hkv <= 128.  Each output row is written by exactly one workgroup with
+ * no atomics on O, so results are bitwise reproducible. */
+ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                            const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                            int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                            int32_t head_dim, const ea_sparsity_params* params, void* O,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EA_H */

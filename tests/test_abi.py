@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: every declared symbol is exported, the workspace
+size is a pure host computation, and every host-checkable error returns its
+status before anything is launched (the pointers below are never
+dereferenced: validation fails first)."""
+import ctypes
+
+import pytest
+
+import full_attention_long_amd as ea
+from full_attention_long_amd import binding as bnd
+
+FAKE = 0x100000  # 256-byte aligned, never dereferenced by a failing call
+
+
+def test_every_header_function_is_exported():
+    names = ea.header_functions()
+    assert set(names) == {"ea_abi_version", "ea_last_error", "ea_route",
+                          "ea_hybrid_prefill_workspace_size", "ea_hybrid_prefill"}
+    L = ea.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert ea.ea_abi_version() == 1
+
+
+def test_workspace_size_bounds():
+    ws = ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
+    vt = 8 * 128 * (131072 + 64) * 2          # transposed V copy (one padding block)
+    items = 2 * 8 * (131072 // 32 + 1) * 16   # raw + sorted work items
+    assert vt + items <= ws <= vt + items + 64 * 1024
+    assert ea.ea_hybrid_prefill_workspace_size(1, 1000, 1000, 32, 8, 128, bnd.EA_F32) > \
+        ea.ea_hybrid_prefill_workspace_size(1, 1000, 1000, 32, 8, 128, bnd.EA_BF16)
+    # invalid sizes -> 0
+    assert ea.ea_hybrid_prefill_workspace_size(0, 1000, 1000, 32, 8, 128, 1) == 0
+    assert ea.ea_hybrid_prefill_workspace_size(1, 1000, 1000, 30, 8, 128, 1) == 0
+    assert ea.ea_hybrid_prefill_workspace_size(1, 1000, 1000, 32, 8, 96, 1) == 0
+    assert ea.ea_hybrid_prefill_workspace_size(1, 2**31, 1000, 32, 8, 128, 1) == 0
+
+
+def _prefill(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=1, modes=FAKE, cu=FAKE, B=1, T=1000, max_seqlen=1000,
+             Hq=8, Hkv=2, d=128, block=64, n_sink=1, window=0, keep=0.2, scale=0.0, O=FAKE,
+             lse=None, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    sp = bnd.SparsityParams(a["block"], a["n_sink"], a["window"], a["keep"], a["scale"])
+    st = ea.lib().ea_hybrid_prefill(a["Q"], a["K"], a["V"], a["dtype"], a["modes"], a["cu"], a["B"],
+                                    a["T"], a["max_seqlen"], a["Hq"], a["Hkv"], a["d"],
+                                    ctypes.byref(sp), a["O"], a["lse"], a["ws"], a["ws_bytes"], None)
+    return st, ea.ea_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Q=None), -1, "null pointer"),
+    (dict(modes=None), -1, "null pointer"),
+    (dict(O=None), -1, "null pointer"),
+    (dict(B=0), -1, "B must be"),
+    (dict(Hq=6, Hkv=4), -1, "multiple of Hkv"),
+    (dict(Hq=256, Hkv=1), -2, "Hq / Hkv"),
+    (dict(d=96), -2, "head_dim"),
+    (dict(dtype=7), -2, "dtype"),
+    (dict(block=128), -2, "block"),
+    (dict(n_sink=-1), -1, "n_sink"),
+    (dict(window=-2), -1, "window_blocks"),
+    (dict(keep=0.0), -1, "keep_fraction"),
+    (dict(keep=1.5), -1, "keep_fraction"),
+    (dict(scale=-1.0), -1, "softmax_scale"),
+    (dict(scale=float("nan")), -1, "softmax_scale"),
+    (dict(max_seqlen=0), -1, "max_seqlen"),
+    (dict(max_seqlen=2000), -1, "max_seqlen"),
+    (dict(T=2**31), -1, "total_tokens"),
+    (dict(ws=None), -3, "workspace"),
+    (dict(ws_bytes=1024), -3, "workspace"),
+    (dict(ws=FAKE + 16), -1, "256-byte"),
+    (dict(Q=FAKE + 2), -1, "16-byte"),
+])
+def test_prefill_host_errors(kw, status, msg):
+    st, err = _prefill(**kw)
+    assert st == status and msg in err, (st, err)
+
+
+def test_prefill_zero_tokens_is_a_no_op():
+    st, err = _prefill(T=0, max_seqlen=0)
+    assert st == 0 and err == ""
+
+
+def _route(**kw):
+    a = dict(K=FAKE, dtype=1, cu=FAKE, B=1, Hkv=8, modes=FAKE, d=128, th=512, rh=64, pool=100,
+             w=FAKE)
+    a.update(kw)
+    desc = bnd.RouterDesc(a["d"], a["th"], a["rh"], a["pool"], *([a["w"]] * 8))
+    st = ea.lib().ea_route(a["K"], a["dtype"], a["cu"], a["B"], a["Hkv"], ctypes.byref(desc),
+                           a["modes"], None, None)
+    return st, ea.ea_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=None), -1, "null pointer"),
+    (dict(modes=None), -1, "null pointer"),
+    (dict(w=None), -1, "router weight"),
+    (dict(B=0), -1, "B and Hkv"),
+    (dict(d=300), -2, "head_dim"),
+    (dict(th=5000), -2, "task_hidden"),
+    (dict(rh=2000), -2, "router_hidden"),
+    (dict(pool=0), -1, "pool_len"),
+    (dict(dtype=3), -2, "dtype"),
+])
+def test_route_host_errors(kw, status, msg):
+    st, err = _route(**kw)
+    assert st == status and msg in err, (st, err)
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(bnd, "_lib", None)
+    monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        bnd.lib()
