@@ -162,10 +162,13 @@ def main():
                     help="comma-separated workload names measured together")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, to scale profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the hybrid prefill "
-              "is measured on one GPU's share; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the hybrid prefill "
+              "runs and is measured on a single GPU's share of the work", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -173,6 +176,14 @@ def main():
     from full_attention_long_amd import metrics
     ea.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * 2**20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+        del src, dst
     runs, cases = [], []
     for name in args.runs.split(","):
         r, c = measure(name, args.steps, args.warmup)

@@ -133,8 +133,7 @@ ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtyp
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
-  if (e == hipSuccess) e = ea::launch_transpose_v(s, V, cu_seqlens, ws, base, hs);
-  if (e == hipSuccess) e = ea::launch_attention(s, g, Q, K, modes, cu_seqlens, O, lse, ws, base, hs);
+  if (e == hipSuccess) e = ea::launch_attention(s, g, Q, K, V, modes, cu_seqlens, O, lse, ws, base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -8,16 +8,26 @@
 // sparse pattern (sink blocks + causal local window, 64-token blocks) and the
 // softmax scale 1/sqrt(d) are the readings stated in ea.h.
 //
-// Work item = query tile of one KV-head group: 128 rows = G heads x BMq
-// positions, one wave per 32 rows.  Each wave computes the transposed score
-// tile S^T = K Q^T (keys x queries) with 32x32 MFMAs so that every lane owns
-// one query row: the row max needs one cross-half exchange per key block and
-// the row sum none until the epilogue.  Probabilities P^T stay in registers in
-// the MFMA result layout and feed O^T += V^T P^T directly; V^T comes from a
-// transposed copy of V whose key order matches that layout.  K and V^T blocks
-// of 64 keys are double-buffered through LDS: the next block's coalesced
-// 16-byte global loads are issued before the current block's MFMAs and land
-// in the other buffer after them, one barrier per block.
+// Work item = query tile of one KV-head group: 256 rows = G heads x BMq
+// positions, one wave per 32 rows, 8 waves per workgroup, so every K/V block
+// brought into LDS serves 256 query rows.  Each wave computes the transposed
+// score tile S^T = K Q^T (keys x queries) with 32x32 MFMAs so that every lane
+// owns one query row: the row max needs one cross-half exchange per key block
+// and the row sum none until the epilogue.  Probabilities P^T stay in
+// registers in the MFMA result layout and feed O^T += V^T P^T directly; the
+// V^T operand is read from the row-major V tile with gfx950's transposing LDS
+// read (ds_read_b64_tr_b16), whose 4-key groups also match the key order the
+// MFMA result leaves in each lane.  K and V blocks of 64 keys are
+// double-buffered through LDS: the next block's coalesced 16-byte global loads
+// are issued before the current block's MFMAs and land in the other buffer
+// after them, one barrier per block.
+//
+// Work-list entries are mapped onto the XCDs in chunks: the hardware hands
+// workgroup i to XCD i mod 8, and workgroup i takes list entry
+// ((j / C) * 8 + i mod 8) * C + j mod C with j = i / 8, C = 8.  The workgroups
+// resident on one XCD then hold runs of consecutive entries, which the sort
+// keeps in query order within a KV head, so they stream the same K/V blocks
+// through that XCD's L2 at about the same time.
 //
 // Online softmax in base 2 (scale * log2 e folded into one FMA per score) with
 // a lazy rescale: the running max only moves, and O and l are only rescaled,
@@ -35,6 +45,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
@@ -43,17 +56,16 @@ constexpr float kMinusBig = -1.0e30f;      // finite "minus infinity" for the ru
 struct AttnArgs {
   const void* Q;
   const void* K;
-  const void* Vt;
+  const void* V;
   void* O;
   float* lse;
   const int8_t* modes;
   const int32_t* cu;
   const int32_t* seq_w;
-  const int32_t* vblk_prefix;
   const Item* items;
+  const int32_t* order;
   const int32_t* meta;
   int64_t T;
-  int64_t tpad;
   int32_t Hq, Hkv, G, BMq, n_sink;
   float scale_log2;
 };
@@ -66,6 +78,12 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Four bf16 of one V column, rows r..r+3 of a 4-row group, per lane of each
+// 16-lane group (gfx950 transposing LDS read).
+__device__ __forceinline__ i16x4 ds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
   f32x8 v;
 #pragma unroll
@@ -74,20 +92,27 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
 }
 
 template <bool BF16, int D>
-__global__ __launch_bounds__(256, BF16 ? 2 : 1) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs a) {
   using E = std::conditional_t<BF16, uint16_t, float>;
+  constexpr int NT = kAttnWaves * 64;      // threads per workgroup
   constexpr int CH = 16 / sizeof(E);       // elements per 16-byte chunk
   constexpr int KROW = D + CH;             // padded LDS row of K (elements)
-  constexpr int VROW = kBlock + CH;        // padded LDS row of V^T (elements)
-  constexpr int NLD = kBlock * D / CH / 256;  // 16-byte chunks per thread per block
+  // padded LDS row of V: 64 bytes of pad put the 4 rows one transposing read
+  // touches on disjoint bank ranges (bf16); the fp32 path reads single words
+  constexpr int VROW = BF16 ? D + 32 : D + CH;
+  constexpr int NLD = kBlock * D / CH / NT;  // 16-byte chunks per thread per block (K and V each)
   constexpr int DT = D / 32;               // 32-wide dim tiles of O^T
-  static_assert(NLD * 256 * CH == kBlock * D, "tile must split evenly over 256 threads");
+  static_assert(NLD * NT * CH == kBlock * D, "tile must split evenly over the workgroup");
 
   __shared__ __attribute__((aligned(16))) E Ks[2][kBlock * KROW];
-  __shared__ __attribute__((aligned(16))) E Vs[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) E Vs[2][kBlock * VROW];
 
-  if (static_cast<int32_t>(blockIdx.x) >= a.meta[kMetaItems]) return;
-  const Item it = a.items[blockIdx.x];
+  // XCD-chunked position in the cost-sorted work list
+  const int64_t wg = blockIdx.x;
+  const int64_t jx = wg / kNumXcd;
+  const int64_t pos_in_list = ((jx / kXcdChunk) * kNumXcd + (wg % kNumXcd)) * kXcdChunk + (jx % kXcdChunk);
+  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
+  const Item it = a.items[a.order[pos_in_list]];
   const int b = it.b, kvh = it.kvh;
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
@@ -118,8 +143,7 @@ __global__ __launch_bounds__(256, BF16 ? 2 : 1) void attention_kernel(AttnArgs a
 
   const E* Qp = static_cast<const E*>(a.Q);
   const E* Kp = static_cast<const E*>(a.K);
-  const E* Vtp = static_cast<const E*>(a.Vt);
-  const int64_t vcol0 = static_cast<int64_t>(a.vblk_prefix[b]) * kBlock;
+  const E* Vp = static_cast<const E*>(a.V);
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   using QFrag = std::conditional_t<BF16, bf16x8, f32x4>;
@@ -142,28 +166,26 @@ __global__ __launch_bounds__(256, BF16 ? 2 : 1) void attention_kernel(AttnArgs a
   auto gload = [&](int kb) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      const int c = n * 256 + tid;
-      const int krow = c / (D / CH), kcol = (c % (D / CH)) * CH;
-      const int key = kb * kBlock + krow;
+      const int c = n * NT + tid;
+      const int row = c / (D / CH), col = (c % (D / CH)) * CH;
+      const int key = kb * kBlock + row;
       if (key < L) {
-        kreg[n] = *reinterpret_cast<const u32x4*>(
-            Kp + (static_cast<int64_t>(tok0 + key) * a.Hkv + kvh) * D + kcol);
+        const int64_t off = (static_cast<int64_t>(tok0 + key) * a.Hkv + kvh) * D + col;
+        kreg[n] = *reinterpret_cast<const u32x4*>(Kp + off);
+        vreg[n] = *reinterpret_cast<const u32x4*>(Vp + off);
       } else {
         kreg[n] = u32x4{0, 0, 0, 0};
+        vreg[n] = u32x4{0, 0, 0, 0};
       }
-      const int vrow = c / (kBlock / CH), vcol = (c % (kBlock / CH)) * CH;
-      vreg[n] = *reinterpret_cast<const u32x4*>(
-          Vtp + (static_cast<int64_t>(kvh) * D + vrow) * a.tpad + vcol0 + kb * kBlock + vcol);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      const int c = n * 256 + tid;
-      const int krow = c / (D / CH), kcol = (c % (D / CH)) * CH;
-      *reinterpret_cast<u32x4*>(&Ks[buf][krow * KROW + kcol]) = kreg[n];
-      const int vrow = c / (kBlock / CH), vcol = (c % (kBlock / CH)) * CH;
-      *reinterpret_cast<u32x4*>(&Vs[buf][vrow * VROW + vcol]) = vreg[n];
+      const int c = n * NT + tid;
+      const int row = c / (D / CH), col = (c % (D / CH)) * CH;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KROW + col]) = kreg[n];
+      *reinterpret_cast<u32x4*>(&Vs[buf][row * VROW + col]) = vreg[n];
     }
   };
   auto kb_of = [&](int n) { return n < r1_end ? n : r2_beg + (n - r1_end); };
@@ -253,29 +275,29 @@ __global__ __launch_bounds__(256, BF16 ? 2 : 1) void attention_kernel(AttnArgs a
       pb[1] = to_bf16x8(s0, 8);
       pb[2] = to_bf16x8(s1, 0);
       pb[3] = to_bf16x8(s1, 8);
+      // lane (group g16 of 16 lanes, i16 within it) reads rows 4h + i16/4 (+16u, +8 for
+      // the upper 4 keys) at columns 16 (g16 & 1) + 4 (i16 & 3) (+32t): the result is
+      // V[16u + 4h + 0..3 (+8)][32t + lq], the A operand for keys in P^T's order
+      const E* vb = &Vs[buf][(4 * h + (lane & 15) / 4) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const E* vrow = &Vs[buf][(32 * t + lq) * VROW + 8 * h];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * u);
-          o[t] = mfma_bf16(vf, pb[u], o[t]);
+          const i16x4 lo = ds_read_tr(vb + 16 * u * VROW + 32 * t);
+          const i16x4 hi = ds_read_tr(vb + (16 * u + 8) * VROW + 32 * t);
+          const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, v8), pb[u], o[t]);
         }
       }
     } else {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const E* vrow = &Vs[buf][(32 * t + lq) * VROW + 8 * h];
+        const E* vcol = &Vs[buf][32 * t + lq];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 va = *reinterpret_cast<const f32x4*>(vrow + 16 * u);
-          const f32x4 vb = *reinterpret_cast<const f32x4*>(vrow + 16 * u + 4);
-          const f32x16& p = (u < 2) ? s0 : s1;
-          const int base = 8 * (u & 1);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[t] = mfma_f32(va[e], p[base + e], o[t]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[t] = mfma_f32(vb[e], p[base + 4 + e], o[t]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * (i / 4) + 4 * h + (i % 4);
+          o[t] = mfma_f32(vcol[key * VROW], s0[i], o[t]);
+          o[t] = mfma_f32(vcol[(key + 32) * VROW], s1[i], o[t]);
         }
       }
     }
@@ -314,35 +336,35 @@ __global__ __launch_bounds__(256, BF16 ? 2 : 1) void attention_kernel(AttnArgs a
 
 template <bool BF16, int D>
 void launch(const AttnArgs& args, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((attention_kernel<BF16, D>), dim3(grid), dim3(256), 0, st, args);
+  hipLaunchKernelGGL((attention_kernel<BF16, D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
-                            const int8_t* modes, const int32_t* cu, void* O, float* lse,
-                            const Workspace& ws, char* base, hipStream_t st) {
+                            const void* V, const int8_t* modes, const int32_t* cu, void* O,
+                            float* lse, const Workspace& ws, char* base, hipStream_t st) {
   AttnArgs a;
   a.Q = Q;
   a.K = K;
-  a.Vt = base + ws.vt;
+  a.V = V;
   a.O = O;
   a.lse = lse;
   a.modes = modes;
   a.cu = cu;
   a.seq_w = reinterpret_cast<const int32_t*>(base + ws.seq_w);
-  a.vblk_prefix = reinterpret_cast<const int32_t*>(base + ws.vblk_prefix);
-  a.items = reinterpret_cast<const Item*>(base + ws.items);
+  a.items = reinterpret_cast<const Item*>(base + ws.items_raw);
+  a.order = reinterpret_cast<const int32_t*>(base + ws.order);
   a.meta = reinterpret_cast<const int32_t*>(base + ws.meta);
   a.T = s.T;
-  a.tpad = ws.tpad;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.G = s.G;
   a.BMq = s.BMq;
   a.n_sink = g.n_sink;
   a.scale_log2 = g.scale_log2;
-  const unsigned grid = static_cast<unsigned>(ws.max_items);
+  constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
+  const unsigned grid = static_cast<unsigned>((ws.max_items + span - 1) / span * span);
   const bool bf16 = s.elem_bytes == 2;
   if (bf16 && s.d == 128) launch<true, 128>(a, grid, st);
   else if (bf16 && s.d == 64) launch<true, 64>(a, grid, st);

@@ -9,8 +9,13 @@
 
 namespace ea {
 
-// Query rows per attention work item: G query heads x (128 / G) positions.
-constexpr int kTileRows = 128;
+// Query rows per attention work item: G query heads x (kTileRows / G) positions,
+// 32 rows per wave of the attention kernel's workgroup.
+constexpr int kTileRows = 256;
+constexpr int kAttnWaves = kTileRows / 32;
+// Consecutive work-list entries given to one XCD before moving to the next.
+constexpr int kXcdChunk = 8;
+constexpr int kNumXcd = 8;
 // Key/value block of the sparse pattern and of the attention inner loop.
 constexpr int kBlock = 64;
 
@@ -24,18 +29,16 @@ struct Item {
 
 // Slots of the small int32 header at the start of the workspace.
 enum Meta : int {
-  kMetaItems = 0,       // number of work items
-  kMetaTiles = 1,       // sum over sequences of ceil(L_b / BMq)
-  kMetaVBlocks = 2,     // sum over sequences of ceil(L_b / 64)
+  kMetaTiles = 0,       // sum over sequences of ceil(L_b / BMq); items = tiles * Hkv
   kMetaSlots = 64
 };
 
 // Byte layout of the workspace, a pure function of the host-visible sizes.
 struct Workspace {
-  size_t meta, tile_prefix, vblk_prefix, seq_w, hist, cursor, items_raw, items, vt, total;
+  size_t meta, tile_prefix, seq_w, keys_in, keys_out, vals_in, order, items_raw, sort_tmp;
+  size_t sort_tmp_bytes, total;
   int64_t max_items;   // bound on work items
-  int64_t tpad;        // row stride (tokens) of the transposed V copy
-  int32_t nbins;       // cost histogram bins
+  int32_t nbins;       // cost bins of the sort key
 };
 
 struct Shape {
@@ -63,11 +66,8 @@ hipError_t launch_route(const void* K, bool bf16, const int32_t* cu, int32_t B, 
 hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,
                            const int32_t* cu, const Workspace& ws, char* base, hipStream_t st);
 
-hipError_t launch_transpose_v(const Shape& s, const void* V, const int32_t* cu,
-                              const Workspace& ws, char* base, hipStream_t st);
-
 hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
-                            const int8_t* modes, const int32_t* cu, void* O, float* lse,
-                            const Workspace& ws, char* base, hipStream_t st);
+                            const void* V, const int8_t* modes, const int32_t* cu, void* O,
+                            float* lse, const Workspace& ws, char* base, hipStream_t st);
 
 }  // namespace ea

@@ -124,8 +124,9 @@ ea_status ea_route(const void* K, ea_dtype dtype, const int32_t* cu_seqlens, int
                    void* stream);
 
 /* Bytes of device workspace ea_hybrid_prefill needs for these sizes (0 if the
- * sizes are invalid).  The workspace holds the per-launch work list and a
- * transposed copy of V; its contents need not be initialised. */
+ * sizes are invalid).  The workspace holds the per-launch work list and its
+ * sort buffers (a few bytes per query tile); its contents need not be
+ * initialised. */
 size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
                                         int32_t Hq, int32_t Hkv, int32_t head_dim,
                                         ea_dtype dtype);
@@ -147,7 +148,7 @@ size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t
  *               (256-byte aligned); not shared between concurrent calls
  *
  * head_dim must be 64 or 128; Hq must be a multiple of Hkv with
- * Hq / Hkv <= 128.  Each output row is written by exactly one workgroup with
+ * Hq / Hkv <= 256.  Each output row is written by exactly one workgroup with
  * no atomics on O, so results are bitwise reproducible. */
 ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
                             const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
