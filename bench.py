@@ -1,19 +1,30 @@
 """Throughput of the routed hybrid attention prefill on one MI355X.
 
-One step = one layer's whole hot path on device-resident inputs: the router
-(boundary pooling, task MLP, router MLP, argmax), the device work list, the
-V transpose and the fused FA/SA attention forward.  The default workload is
-the 128K-token Qwen3-4B-shaped layer (32 query heads, 8 KV heads, d = 128,
-bf16), measured in both routing mixes it is specified with (2 of 8 and 6 of 8
-KV heads sparse); `value` is the combined effective TFLOP/s of the two
-layers: their effective FLOPs over their summed step times.  Effective FLOPs
-count only the computed 64 x 64 FA/SA blocks.
+One step = the whole hot path of one transformer layer's attention, run once
+for each routing mix of the headline workload, on inputs already resident in
+device memory: the router (boundary pooling, task MLP, router MLP, argmax),
+the cost-ordered work list, and the fused FA/SA attention forward.  The
+headline workload is the 128K-token Qwen3-4B-shaped layer (32 query heads, 8
+KV heads, d = 128, bf16, one sequence) in its two routing mixes, 2 of 8 and 6
+of 8 KV heads sparse, so one step is two layers.  `value` is effective TFLOP/s
+over the whole step: the effective FLOPs of both layers (only the computed
+64 x 64 FA/SA blocks count, the router's few MFLOP do not) over the step time.
 
-Prints one JSON line.  --gpus must be 1 (the path runs on one GPU).
+`roofline` is the attention kernel alone: its effective FLOPs per launch over
+its average launch time, from HIP events recorded on the stream it runs on,
+against the MI355X dense bf16 MFMA peak.  `traffic` is that kernel's HBM bytes
+per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by what the
+same counters read for an elementwise kernel of known size), read from
+profiles/attention_traffic.json when it was taken on the current kernel
+source, else null.
+
+Prints one JSON line.  --gpus must be 1: the path is measured on one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -28,95 +39,86 @@ if ROOT not in sys.path:
 
 METRIC = "hybrid prefill effective TFLOP/s + ms/layer at 128K; % bf16 MFMA roofline"
 DEFAULT_RUNS = ["qwen4b_s128k_sa2", "qwen4b_s128k_sa6"]
+ATTN_SRC = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attention.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_KERNEL = "attention_kernel"
+CALIB_KERNEL = "bitwise_not"
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def device_inputs(case):
-    import torch
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
-    return {
-        "q": dev(case.q), "k": dev(case.k), "v": dev(case.v),
-        "cu": torch.from_numpy(case.cu_seqlens).cuda(),
-        "w": {n: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
-              for n, a in case.weights.items()},
-    }
+def kernel_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measure(name, steps, warmup):
-    import torch
+class Layer:
+    """One routed layer's device-resident inputs, outputs and workspace."""
 
-    import full_attention_long_amd as ea
-    from full_attention_long_amd import metrics
-    from workloads import gen
-    from workloads.configs import WORKLOADS
+    def __init__(self, name):
+        import torch
 
-    wl = WORKLOADS[name]
-    log(f"{name}: generating inputs")
-    case = gen.build_case(wl)
-    dv = device_inputs(case)
-    T, Hq, Hkv, d = case.T, case.Hq, case.Hkv, case.d
-    maxlen = int(case.lengths.max())
-    O = torch.empty_like(dv["q"])
-    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
-    modes = torch.empty((case.B, Hkv), dtype=torch.int8, device="cuda")
-    logits = torch.empty((case.B, Hkv, 2), dtype=torch.float32, device="cuda")
-    ws = torch.empty(ea.ea_hybrid_prefill_workspace_size(case.B, T, maxlen, Hq, Hkv, d, 1),
-                     dtype=torch.uint8, device="cuda")
+        import full_attention_long_amd as ea
+        from workloads import gen
+        from workloads.configs import WORKLOADS
 
-    def step(ev=None):
-        ea.ea_route(dv["k"], dv["cu"], dv["w"], pool_len=case.pool_len, modes=modes, logits=logits)
+        self.name = name
+        log(f"{name}: generating inputs")
+        self.case = c = gen.build_case(WORKLOADS[name])
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+        self.q, self.k, self.v = bf(c.q), bf(c.k), bf(c.v)
+        self.cu = torch.from_numpy(c.cu_seqlens).cuda()
+        self.w = {n: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+                  for n, a in c.weights.items()}
+        self.maxlen = int(c.lengths.max())
+        self.O = torch.empty_like(self.q)
+        self.lse = torch.empty((c.Hq, c.T), dtype=torch.float32, device="cuda")
+        self.modes = torch.empty((c.B, c.Hkv), dtype=torch.int8, device="cuda")
+        self.logits = torch.empty((c.B, c.Hkv, 2), dtype=torch.float32, device="cuda")
+        nbytes = ea.ea_hybrid_prefill_workspace_size(c.B, c.T, self.maxlen, c.Hq, c.Hkv, c.d, 1)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.geom = dict(n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+
+    def step(self, ev=None):
+        """Router, work list, attention; ev = 4 events bracketing route / plan / run."""
+        import full_attention_long_amd as ea
+        c = self.case
         if ev is not None:
             ev[0].record()
-        ea.ea_hybrid_prefill(dv["q"], dv["k"], dv["v"], modes, dv["cu"], maxlen, n_sink=case.n_sink,
-                             keep_fraction=case.keep_fraction, out=O, lse=lse, workspace=ws)
+        ea.ea_route(self.k, self.cu, self.w, pool_len=c.pool_len, modes=self.modes,
+                    logits=self.logits)
         if ev is not None:
             ev[1].record()
-
-    log(f"{name}: warmup {warmup}")
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    m = modes.cpu().numpy()
-    assert np.array_equal(m, case.target_modes), "routing differs from the workload's target"
-    ef = metrics.effective_flops(m, case.lengths, Hq, Hkv, d, n_sink=case.n_sink,
-                                 keep_fraction=case.keep_fraction)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"{name}: timing {steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        step(evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = start.elapsed_time(stop) / steps
-    prefill_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    log(f"{name}: {step_ms:.3f} ms/step, prefill call {prefill_ms:.3f} ms, wall {wall:.2f} s")
-    res = {
-        "workload": name, "seq_len": int(maxlen), "tokens": int(T), "Hq": Hq, "Hkv": Hkv, "d": d,
-        "sa_kv_heads": int(m.sum()), "msr": metrics.msr(m), "n_sink": case.n_sink,
-        "keep_fraction": case.keep_fraction, "effective_flops": int(ef),
-        "ms_per_layer": step_ms, "prefill_ms": prefill_ms,
-        "effective_tflops": ef / (step_ms * 1e-3) / 1e12,
-        "prefill_effective_tflops": ef / (prefill_ms * 1e-3) / 1e12,
-        "seed": case.seed,
-    }
-    res["pct_bf16_roofline"] = 100.0 * res["effective_tflops"] / metrics.MI355X_BF16_DENSE_TFLOPS
-    del dv, O, lse, ws
-    torch.cuda.empty_cache()
-    return res, case
+        ea.ea_hybrid_prefill_plan(self.modes, self.cu, c.T, self.maxlen, c.Hq, c.Hkv, c.d, 1,
+                                  self.ws, **self.geom)
+        if ev is not None:
+            ev[2].record()
+        ea.ea_hybrid_prefill_run(self.q, self.k, self.v, self.modes, self.cu, self.maxlen, self.ws,
+                                 out=self.O, lse=self.lse, **self.geom)
+        if ev is not None:
+            ev[3].record()
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The oracle on a bounded sample of the same layer: 64-row query blocks of
-    one query head per KV head, at seeded positions, until ~budget_s of CPU time
-    has been spent; effective FLOPs of the sample over its wall time."""
+def stored_traffic():
+    """HBM bytes per attention launch per workload from the stored counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t
+
+
+def cpu_baseline(cases, budget_s=12.0):
+    """The oracle on a bounded sample of the same layers: 64-row query blocks
+    of one query head at seeded positions, alternating between the layers,
+    until ~budget_s of CPU time is spent; effective FLOPs of the sample over
+    its wall time."""
     from full_attention_long_amd import metrics
     from oracle import ea_oracle as orc
 
@@ -125,32 +127,83 @@ def cpu_baseline(case, budget_s=12.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    L = int(case.lengths[0])
-    G = case.Hq // case.Hkv
-    modes = case.target_modes
-    w = metrics.window_blocks(L, case.n_sink, case.keep_fraction)
     rng = np.random.default_rng(0)
-    qf, kf, vf = case.q_f32(), case.k_f32(), case.v_f32()
+    f32 = [(c.q_f32(), c.k_f32(), c.v_f32()) for c in cases]
     done_flops, units, t_used = 0, 0, 0.0
-    while t_used < budget_s and units < 256:
-        g = units % case.Hkv
-        hq = g * G + (units // case.Hkv) % G
+    while t_used < budget_s and units < 512:
+        ci = units % len(cases)
+        c = cases[ci]
+        qf, kf, vf = f32[ci]
+        L = int(c.lengths[0])
+        G = c.Hq // c.Hkv
+        w = metrics.window_blocks(L, c.n_sink, c.keep_fraction)
+        g = (units // len(cases)) % c.Hkv
+        hq = g * G + (units // (len(cases) * c.Hkv)) % G
         qb = int(rng.integers(0, L // 64))
         toks = np.arange(qb * 64, min(L, qb * 64 + 64))
         t0 = time.perf_counter()
-        orc.hybrid_attention_rows(qf, kf, vf, modes, case.cu_seqlens, toks, [hq],
-                                  n_sink=case.n_sink, keep_fraction=case.keep_fraction)
+        orc.hybrid_attention_rows(qf, kf, vf, c.target_modes, c.cu_seqlens, toks, [hq],
+                                  n_sink=c.n_sink, keep_fraction=c.keep_fraction)
         t_used += time.perf_counter() - t0
-        nvis = qb + 1 if modes[0, g] == 0 else min(qb + 1, case.n_sink + w)
-        done_flops += 4 * case.d * len(toks) * 64 * nvis
+        nvis = qb + 1 if c.target_modes[0, g] == 0 else min(qb + 1, c.n_sink + w)
+        done_flops += 4 * c.d * len(toks) * 64 * nvis
         units += 1
     return {
-        "value": done_flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+        "value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{units} query blocks of 64 rows (one query head each, seeded positions) of "
-                  f"{case.name}; float64 two-pass softmax; {t_used:.1f} s; "
-                  f"cpu {platform.processor() or platform.machine()}",
+        "sample": f"{units} query blocks of 64 rows x one query head at seeded positions, "
+                  f"alternating {'+'.join(c.name for c in cases)}; float64 two-pass softmax over "
+                  f"the visible keys; {t_used:.1f} s of CPU; {platform.machine()} host",
     }
+
+
+def calibrate(mib):
+    """One elementwise kernel of known traffic (reads and writes mib MiB), so
+    that profiler byte counters can be scaled to bytes."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"calibration: {CALIB_KERNEL} over {n * 4} bytes in, {n * 4} bytes out")
+    del src, dst
+
+
+def summarize_counters(pmc_dirs, calib_mib, layers_flops, out_path):
+    """Turn rocprofv3 --pmc CSV output (one directory per counter) into the
+    stored traffic summary: mean KiB per attention dispatch per counter, scaled
+    by expected / measured KiB of the calibration kernel."""
+    import csv
+    res = {}
+    for d in pmc_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = []
+        for fn in files:
+            with open(fn) as f:
+                rows += list(csv.DictReader(f))
+        for counter in {r["Counter_Name"] for r in rows}:
+            att = [float(r["Counter_Value"]) for r in rows
+                   if r["Counter_Name"] == counter and ATTN_KERNEL in r["Kernel_Name"]]
+            cal = [float(r["Counter_Value"]) for r in rows
+                   if r["Counter_Name"] == counter and CALIB_KERNEL in r["Kernel_Name"]]
+            if not att or not cal:
+                raise SystemExit(f"{counter}: attention {len(att)} / calibration {len(cal)} rows")
+            factor = calib_mib * 1024.0 / (sum(cal) / len(cal))
+            res[counter] = {"attention_kib_per_dispatch": sum(att) / len(att),
+                            "dispatches": len(att), "calibration_kib": sum(cal) / len(cal),
+                            "expected_calibration_kib": calib_mib * 1024.0, "scale": factor,
+                            "bytes_per_dispatch": sum(att) / len(att) * 1024.0 * factor}
+    total = sum(v["bytes_per_dispatch"] for v in res.values())
+    out = {"kernel": ATTN_KERNEL, "kernel_source_sha256_16": kernel_source_hash(),
+           "counters": res, "hbm_bytes_per_launch": total, "layers": layers_flops}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -159,13 +212,20 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--runs", default=",".join(DEFAULT_RUNS),
-                    help="comma-separated workload names measured together")
+                    help="comma-separated workload names; one step runs each once")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="first run one plain device-to-device copy of this many MiB (a kernel of "
-                         "known traffic, to scale profiler byte counters)")
+    ap.add_argument("--calibrate-mib", type=int, default=0,
+                    help="first run one elementwise kernel that reads and writes this many MiB "
+                         "(for scaling profiler byte counters)")
+    ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="PMC_DIR",
+                    help="no GPU work: turn rocprofv3 --pmc output directories of a run made with "
+                         "--calibrate-mib into profiles/attention_traffic.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.calibrate_mib or 1024, args.runs,
+                           TRAFFIC_JSON)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the hybrid prefill "
               "runs and is measured on a single GPU's share of the work", file=sys.stderr)
@@ -176,46 +236,93 @@ def main():
     from full_attention_long_amd import metrics
     ea.lib()
     torch.cuda.set_device(0)
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib * 2**20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {n} bytes done")
-        del src, dst
-    runs, cases = [], []
-    for name in args.runs.split(","):
-        r, c = measure(name, args.steps, args.warmup)
-        runs.append(r)
-        cases.append(c)
-    tot_ef = sum(r["effective_flops"] for r in runs)
-    tot_ms = sum(r["ms_per_layer"] for r in runs)
-    tot_prefill = sum(r["prefill_ms"] for r in runs)
-    value = tot_ef / (tot_ms * 1e-3) / 1e12
-    achieved = tot_ef / (tot_prefill * 1e-3) / 1e12
+    if args.calibrate_mib:
+        calibrate(args.calibrate_mib)
+    layers = [Layer(n) for n in args.runs.split(",")]
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for ly in layers:
+            ly.step()
+    torch.cuda.synchronize()
+    efs = []
+    for ly in layers:
+        m = ly.modes.cpu().numpy()
+        c = ly.case
+        assert np.array_equal(m, c.target_modes), f"{ly.name}: routing differs from the target"
+        efs.append(metrics.effective_flops(m, c.lengths, c.Hq, c.Hkv, c.d, n_sink=c.n_sink,
+                                           keep_fraction=c.keep_fraction))
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[[E() for _ in range(4)] for _ in layers] for _ in range(args.steps)]
+    start, stop = E(), E()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        for li, ly in enumerate(layers):
+            ly.step(evs[s][li])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(stop) / args.steps
+
+    runs = []
+    for li, ly in enumerate(layers):
+        c = ly.case
+        seg = np.array([[evs[s][li][k].elapsed_time(evs[s][li][k + 1]) for k in range(3)]
+                        for s in range(args.steps)])
+        route_ms, plan_ms, attn_ms = seg.mean(axis=0)
+        layer_ms = float(seg.sum(axis=1).mean())
+        m = ly.modes.cpu().numpy()
+        runs.append({
+            "workload": ly.name, "seq_len": ly.maxlen, "tokens": int(c.T), "Hq": c.Hq,
+            "Hkv": c.Hkv, "d": c.d, "sa_kv_heads": int(m.sum()), "msr": metrics.msr(m),
+            "n_sink": c.n_sink, "keep_fraction": c.keep_fraction,
+            "effective_flops": int(efs[li]), "ms_per_layer": round(layer_ms, 4),
+            "route_ms": round(float(route_ms), 4), "plan_ms": round(float(plan_ms), 4),
+            "attention_ms": round(float(attn_ms), 4),
+            "effective_tflops": round(efs[li] / (layer_ms * 1e-3) / 1e12, 3),
+            "attention_tflops": round(efs[li] / (attn_ms * 1e-3) / 1e12, 3),
+            "seed": c.seed,
+        })
+        log(f"{ly.name}: layer {layer_ms:.3f} ms (route {route_ms:.3f}, plan {plan_ms:.3f}, "
+            f"attention {attn_ms:.3f}) -> {runs[-1]['effective_tflops']:.1f} TFLOP/s")
+    tot_ef = float(sum(efs))
+    value = tot_ef / (step_ms * 1e-3) / 1e12
+    attn_sum = sum(r["attention_ms"] for r in runs)
+    achieved = tot_ef / (attn_sum * 1e-3) / 1e12
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
+    tr = stored_traffic()
+    traffic = None
+    if tr is not None:
+        traffic = round(float(tr["hbm_bytes_per_launch"]), 0)
+    log(f"step {step_ms:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
+        f"attention {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of peak")
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tot_ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "+".join(r["workload"] for r in runs),
-            "layers_per_step": len(runs),
-            "pct_bf16_roofline": round(100 * value / metrics.MI355X_BF16_DENSE_TFLOPS, 2),
+            "workload": "+".join(ly.name for ly in layers),
+            "layers_per_step": len(layers),
+            "ms_per_layer": round(step_ms / len(layers), 4),
+            "pct_bf16_roofline": round(100 * value / peak, 2),
             "runs": runs,
         },
         "roofline": {
-            "bound": "mfma", "achieved": round(achieved, 3),
-            "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / metrics.MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
-            "kernel": "attention_kernel<bf16, 128> (timed as the ea_hybrid_prefill call: work "
-                      "list + V transpose + attention)",
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": "attention_kernel<bf16, 128>",
+            "avg_launch_ms": round(attn_sum / len(runs), 4),
+            "flops_per_launch": round(tot_ef / len(runs), 0),
         },
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(cases[-1], args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline([ly.case for ly in layers], args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

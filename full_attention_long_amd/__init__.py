@@ -8,6 +8,8 @@ from .binding import (  # noqa: F401
     EAError,
     ea_abi_version,
     ea_hybrid_prefill,
+    ea_hybrid_prefill_plan,
+    ea_hybrid_prefill_run,
     ea_hybrid_prefill_workspace_size,
     ea_last_error,
     ea_route,

@@ -68,6 +68,12 @@ def lib() -> ctypes.CDLL:
     L.ea_hybrid_prefill.restype = i32
     L.ea_hybrid_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                     ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
+    L.ea_hybrid_prefill_plan.restype = i32
+    L.ea_hybrid_prefill_plan.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                         ctypes.POINTER(SparsityParams), vp, sz, vp]
+    L.ea_hybrid_prefill_run.restype = i32
+    L.ea_hybrid_prefill_run.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                        ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -143,11 +149,7 @@ def ea_hybrid_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_
                                                       head_dim, dtype_code))
 
 
-def ea_hybrid_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: int = 1,
-                      window_blocks: int = 0, keep_fraction: float = 0.2,
-                      softmax_scale: float = 0.0, block: int = 64, out=None, lse=None,
-                      with_lse: bool = True, workspace=None, stream=None):
-    """O [T, Hq, d] (and LSE float32 [Hq, T]) of the fused hybrid attention forward."""
+def _prefill_args(Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen):
     import torch
     for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (modes, "modes"), (cu_seqlens, "cu_seqlens")]:
         _dev(t, n)
@@ -159,11 +161,53 @@ def ea_hybrid_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: in
         out = torch.empty_like(Q)
     if lse is None and with_lse:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=Q.device)
-    need = ea_hybrid_prefill_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
     if workspace is None:
+        need = ea_hybrid_prefill_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    return T, Hq, Hkv, d, B, code, out, lse, workspace
+
+
+def ea_hybrid_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: int = 1,
+                      window_blocks: int = 0, keep_fraction: float = 0.2,
+                      softmax_scale: float = 0.0, block: int = 64, out=None, lse=None,
+                      with_lse: bool = True, workspace=None, stream=None):
+    """O [T, Hq, d] (and LSE float32 [Hq, T]) of the fused hybrid attention forward."""
+    T, Hq, Hkv, d, B, code, out, lse, workspace = _prefill_args(
+        Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen)
     sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
     _check(lib().ea_hybrid_prefill(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes), _ptr(cu_seqlens),
                                    B, T, max_seqlen, Hq, Hkv, d, ctypes.byref(sp), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def ea_hybrid_prefill_plan(modes, cu_seqlens, total_tokens: int, max_seqlen: int, Hq: int, Hkv: int,
+                           head_dim: int, dtype_code: int, workspace, *, n_sink: int = 1,
+                           window_blocks: int = 0, keep_fraction: float = 0.2,
+                           softmax_scale: float = 0.0, block: int = 64, stream=None):
+    """Build the cost-ordered work list into ``workspace`` (a uint8 device tensor)."""
+    _dev(modes, "modes")
+    _dev(cu_seqlens, "cu_seqlens")
+    _dev(workspace, "workspace")
+    B = cu_seqlens.numel() - 1
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    _check(lib().ea_hybrid_prefill_plan(_ptr(modes), _ptr(cu_seqlens), B, total_tokens, max_seqlen,
+                                        Hq, Hkv, head_dim, dtype_code, ctypes.byref(sp),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def ea_hybrid_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace, *,
+                          n_sink: int = 1, window_blocks: int = 0, keep_fraction: float = 0.2,
+                          softmax_scale: float = 0.0, block: int = 64, out=None, lse=None,
+                          with_lse: bool = True, stream=None):
+    """The attention launch alone, over a workspace ``ea_hybrid_prefill_plan`` filled."""
+    _dev(workspace, "workspace")
+    T, Hq, Hkv, d, B, code, out, lse, workspace = _prefill_args(
+        Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    _check(lib().ea_hybrid_prefill_run(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes),
+                                       _ptr(cu_seqlens), B, T, max_seqlen, Hq, Hkv, d,
+                                       ctypes.byref(sp), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
     return out, lse

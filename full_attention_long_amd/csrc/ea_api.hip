@@ -55,6 +55,44 @@ ea_status check_shape(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int3
   return EA_OK;
 }
 
+// Shared validation of the plan, run and one-shot prefill calls.
+ea_status check_prefill(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                        int32_t d, ea_dtype dtype, const ea_sparsity_params* p, const void* modes,
+                        const void* cu_seqlens, const void* workspace, size_t workspace_bytes,
+                        ea::Shape* s, ea::Workspace* ws, ea::Geometry* g) {
+  ea_status st = check_shape(B, T, max_seqlen, Hq, Hkv, d, dtype, s);
+  if (st != EA_OK) return st;
+  if (!p) return fail(EA_ERR_INVALID_ARG, "null sparsity params");
+  if (p->block != ea::kBlock)
+    return fail(EA_ERR_UNSUPPORTED, "sparsity block must be %d (got %d)", ea::kBlock, p->block);
+  if (p->n_sink_blocks < 0) return fail(EA_ERR_INVALID_ARG, "n_sink_blocks must be >= 0");
+  if (p->window_blocks < 0) return fail(EA_ERR_INVALID_ARG, "window_blocks must be >= 0");
+  if (p->window_blocks == 0 && !(p->keep_fraction > 0.f && p->keep_fraction <= 1.f))
+    return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1] (got %g)", (double)p->keep_fraction);
+  if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+    return fail(EA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!modes || !cu_seqlens) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  *ws = ea::plan_workspace(*s);
+  if (!workspace || workspace_bytes < ws->total)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", ws->total,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  g->n_sink = p->n_sink_blocks;
+  g->window_blocks = p->window_blocks;
+  g->keep_fraction = p->keep_fraction;
+  g->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(static_cast<float>(d));
+  g->scale_log2 = g->scale * 1.44269504088896340736f;
+  return EA_OK;
+}
+
+ea_status check_tensors(const void* Q, const void* K, const void* V, const void* O) {
+  if (!Q || !K || !V || !O) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(EA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+  return EA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,42 +132,57 @@ size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t
   return ea::plan_workspace(s).total;
 }
 
+ea_status ea_hybrid_prefill_plan(const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                                 int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
+                                 int32_t Hkv, int32_t head_dim, ea_dtype dtype,
+                                 const ea_sparsity_params* p, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  ea_status st = check_prefill(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, modes,
+                               cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
+  if (total_tokens == 0) return ok();
+  hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, static_cast<char*>(workspace),
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "work-list launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                                const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                                int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                                int32_t head_dim, const ea_sparsity_params* p, void* O, float* lse,
+                                const void* workspace, size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  ea_status st = check_prefill(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, modes,
+                               cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
+  if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
+  if (total_tokens == 0) return ok();
+  hipError_t e = ea::launch_attention(s, g, Q, K, V, modes, cu_seqlens, O, lse, ws,
+                                      static_cast<char*>(const_cast<void*>(workspace)),
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
                             const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
                             int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
                             int32_t head_dim, const ea_sparsity_params* p, void* O, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream) {
   ea::Shape s;
-  ea_status st = check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s);
-  if (st != EA_OK) return st;
-  if (!p) return fail(EA_ERR_INVALID_ARG, "null sparsity params");
-  if (p->block != ea::kBlock)
-    return fail(EA_ERR_UNSUPPORTED, "sparsity block must be %d (got %d)", ea::kBlock, p->block);
-  if (p->n_sink_blocks < 0) return fail(EA_ERR_INVALID_ARG, "n_sink_blocks must be >= 0");
-  if (p->window_blocks < 0) return fail(EA_ERR_INVALID_ARG, "window_blocks must be >= 0");
-  if (p->window_blocks == 0 && !(p->keep_fraction > 0.f && p->keep_fraction <= 1.f))
-    return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1] (got %g)", (double)p->keep_fraction);
-  if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
-    return fail(EA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (!Q || !K || !V || !modes || !cu_seqlens || !O)
-    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
-    return fail(EA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
-  const ea::Workspace ws = ea::plan_workspace(s);
-  if (!workspace || workspace_bytes < ws.total)
-    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", ws.total,
-                workspace ? workspace_bytes : (size_t)0);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(EA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (total_tokens == 0) return ok();
-
+  ea::Workspace ws;
   ea::Geometry g;
-  g.n_sink = p->n_sink_blocks;
-  g.window_blocks = p->window_blocks;
-  g.keep_fraction = p->keep_fraction;
-  g.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
-  g.scale_log2 = g.scale * 1.44269504088896340736f;
-
+  ea_status st = check_prefill(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, modes,
+                               cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
+  if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
+  if (total_tokens == 0) return ok();
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);

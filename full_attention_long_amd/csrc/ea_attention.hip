@@ -66,7 +66,7 @@ struct AttnArgs {
   const int32_t* order;
   const int32_t* meta;
   int64_t T;
-  int32_t Hq, Hkv, G, BMq, n_sink;
+  int32_t Hq, Hkv, G, BMq, n_sink, stamp;
   float scale_log2;
 };
 
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
   const int64_t wg = blockIdx.x;
   const int64_t jx = wg / kNumXcd;
   const int64_t pos_in_list = ((jx / kXcdChunk) * kNumXcd + (wg % kNumXcd)) * kXcdChunk + (jx % kXcdChunk);
+  if (a.meta[kMetaStamp] != a.stamp) return;  // workspace not planned for these sizes
   if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
   const Item it = a.items[a.order[pos_in_list]];
   const int b = it.b, kvh = it.kvh;
@@ -362,6 +363,7 @@ hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, co
   a.G = s.G;
   a.BMq = s.BMq;
   a.n_sink = g.n_sink;
+  a.stamp = plan_stamp(s);
   a.scale_log2 = g.scale_log2;
   constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
   const unsigned grid = static_cast<unsigned>((ws.max_items + span - 1) / span * span);

@@ -30,6 +30,7 @@ struct Item {
 // Slots of the small int32 header at the start of the workspace.
 enum Meta : int {
   kMetaTiles = 0,       // sum over sequences of ceil(L_b / BMq); items = tiles * Hkv
+  kMetaStamp = 1,       // plan_stamp() of the sizes the list was built for
   kMetaSlots = 64
 };
 
@@ -49,6 +50,20 @@ struct Shape {
 };
 
 Workspace plan_workspace(const Shape& s);
+
+// A 31-bit fingerprint of the sizes a work list is built for.  The planner
+// writes it into the workspace header and the attention kernel does nothing
+// unless it finds the fingerprint of its own sizes there, so a run over an
+// unplanned (or differently planned) workspace never reads a stale list.
+inline int32_t plan_stamp(const Shape& s) {
+  uint64_t h = 0x9E3779B97F4A7C15ull;
+  const int64_t v[6] = {s.B, s.T, s.Hq, s.Hkv, s.BMq, s.max_seqlen};
+  for (int64_t x : v) {
+    h ^= static_cast<uint64_t>(x) + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xBF58476D1CE4E5B9ull;
+  }
+  return static_cast<int32_t>((h >> 33) | 1u);
+}
 
 struct Geometry {
   int32_t n_sink;

@@ -65,8 +65,8 @@ __device__ int32_t block_exclusive_scan(int32_t* a, int64_t n, int32_t* tmp /* [
 // Per-sequence query tiles and sparse window.
 __global__ __launch_bounds__(kScanThreads) void setup_kernel(
     const int32_t* __restrict__ cu, int32_t B, int32_t BMq, int32_t n_sink, int32_t window_blocks,
-    float keep_fraction, int32_t* __restrict__ meta, int32_t* __restrict__ tile_prefix,
-    int32_t* __restrict__ seq_w) {
+    float keep_fraction, int32_t stamp, int32_t* __restrict__ meta,
+    int32_t* __restrict__ tile_prefix, int32_t* __restrict__ seq_w) {
   __shared__ int32_t tmp[kScanThreads / 64 + 1];
   for (int b = threadIdx.x; b < B; b += kScanThreads) {
     const int L = max(0, cu[b + 1] - cu[b]);
@@ -86,6 +86,7 @@ __global__ __launch_bounds__(kScanThreads) void setup_kernel(
   if (threadIdx.x == 0) {
     tile_prefix[B] = tiles;
     meta[kMetaTiles] = tiles;
+    meta[kMetaStamp] = stamp;
   }
 }
 
@@ -185,7 +186,7 @@ hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* mode
   int32_t* order = reinterpret_cast<int32_t*>(base + ws.order);
   Item* raw = reinterpret_cast<Item*>(base + ws.items_raw);
   hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(kScanThreads), 0, st, cu, s.B, s.BMq, g.n_sink,
-                     g.window_blocks, g.keep_fraction, meta, tile_prefix, seq_w);
+                     g.window_blocks, g.keep_fraction, plan_stamp(s), meta, tile_prefix, seq_w);
   const unsigned grid = static_cast<unsigned>((ws.max_items + 255) / 256);
   hipLaunchKernelGGL(items_kernel, dim3(grid), dim3(256), 0, st, cu, modes, s.B, s.Hkv, s.BMq,
                      g.n_sink, meta, tile_prefix, seq_w, ws.nbins, ws.max_items, raw, keys_in,

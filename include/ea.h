@@ -156,6 +156,36 @@ ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtyp
                             int32_t head_dim, const ea_sparsity_params* params, void* O,
                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ea_hybrid_prefill_plan / ea_hybrid_prefill_run - the two halves of
+ * ea_hybrid_prefill, for callers that time or reuse them separately.
+ *
+ * plan builds the cost-ordered work list of (sequence, KV-head group, query
+ * tile) items into `workspace`: each item's cost is its number of visible
+ * 64-key blocks (all causal blocks for an FA head, sink blocks plus the local
+ * window for an SA head), and the list runs most expensive first, so FA and SA
+ * tiles load-balance in the single fused launch (summary Sec. 2.3: one pass
+ * over all routed heads, no splitting or recombining of tensors).  It reads
+ * only modes and cu_seqlens.
+ *
+ * run launches the fused attention forward over a workspace that plan filled
+ * with the same modes, cu_seqlens, sizes and params, on the same stream or
+ * after it; the list is not modified, so one plan serves any number of runs
+ * over different Q, K, V with that routing.  Arguments, errors and outputs are
+ * those of ea_hybrid_prefill; a workspace that was not planned for these
+ * arguments is a precondition violation (not detected). */
+ea_status ea_hybrid_prefill_plan(const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                                 int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
+                                 int32_t Hkv, int32_t head_dim, ea_dtype dtype,
+                                 const ea_sparsity_params* params, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                                const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                                int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                                int32_t head_dim, const ea_sparsity_params* params, void* O,
+                                float* lse, const void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

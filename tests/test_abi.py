@@ -15,7 +15,8 @@ FAKE = 0x100000  # 256-byte aligned, never dereferenced by a failing call
 def test_every_header_function_is_exported():
     names = ea.header_functions()
     assert set(names) == {"ea_abi_version", "ea_last_error", "ea_route",
-                          "ea_hybrid_prefill_workspace_size", "ea_hybrid_prefill"}
+                          "ea_hybrid_prefill_workspace_size", "ea_hybrid_prefill",
+                          "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -114,3 +115,26 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         bnd.lib()
+
+
+def test_plan_and_run_host_errors():
+    L = ea.lib()
+    sp = bnd.SparsityParams(64, 1, 0, 0.2, 0.0)
+    # plan: null modes, bad block, small workspace
+    assert L.ea_hybrid_prefill_plan(None, FAKE, 1, 1000, 1000, 8, 2, 128, 1, ctypes.byref(sp),
+                                    FAKE, 1 << 40, None) == -1
+    assert "null pointer" in ea.ea_last_error()
+    bad = bnd.SparsityParams(32, 1, 0, 0.2, 0.0)
+    assert L.ea_hybrid_prefill_plan(FAKE, FAKE, 1, 1000, 1000, 8, 2, 128, 1, ctypes.byref(bad),
+                                    FAKE, 1 << 40, None) == -2
+    assert L.ea_hybrid_prefill_plan(FAKE, FAKE, 1, 1000, 1000, 8, 2, 128, 1, ctypes.byref(sp),
+                                    FAKE, 16, None) == -3
+    # run: null Q, misaligned O
+    assert L.ea_hybrid_prefill_run(None, FAKE, FAKE, 1, FAKE, FAKE, 1, 1000, 1000, 8, 2, 128,
+                                   ctypes.byref(sp), FAKE, None, FAKE, 1 << 40, None) == -1
+    assert L.ea_hybrid_prefill_run(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, 1000, 1000, 8, 2, 128,
+                                   ctypes.byref(sp), FAKE + 4, None, FAKE, 1 << 40, None) == -1
+    assert "16-byte" in ea.ea_last_error()
+    # zero tokens: nothing to do
+    assert L.ea_hybrid_prefill_plan(FAKE, FAKE, 1, 0, 0, 8, 2, 128, 1, ctypes.byref(sp),
+                                    FAKE, 1 << 40, None) == 0

@@ -230,3 +230,37 @@ def test_full_size_sampled(name):
     compare_o(got, ref, c.dtype)
     assert np.abs(got_lse - ref_lse).max() <= LSE_TOL
     assert bool(torch.isfinite(O).all())
+
+
+def test_plan_then_run_equals_one_shot_and_plan_is_reusable():
+    import full_attention_long_amd as ea
+    from gpu_helpers import max_seqlen
+    c = gen.custom_case(13, [1500, 0, 700], 8, 2, 128, "bf16")
+    modes = np.array([[1, 0], [0, 1], [0, 1]], np.int8)
+    note("plan/run vs one-shot")
+    one, lone = gpu_prefill(c, modes)
+    dv = to_device(c)
+    m = torch.from_numpy(modes).cuda()
+    n = ea.ea_hybrid_prefill_workspace_size(c.B, c.T, max_seqlen(c), c.Hq, c.Hkv, c.d, 1)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ea.ea_hybrid_prefill_plan(m, dv["cu"], c.T, max_seqlen(c), c.Hq, c.Hkv, c.d, 1, ws)
+    for _ in range(2):
+        o, l = ea.ea_hybrid_prefill_run(dv["q"], dv["k"], dv["v"], m, dv["cu"], max_seqlen(c), ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, one) and torch.equal(l, lone)
+
+
+def test_run_over_unplanned_workspace_writes_nothing():
+    import full_attention_long_amd as ea
+    from gpu_helpers import max_seqlen
+    c = gen.custom_case(14, [900], 8, 2, 128, "bf16")
+    dv = to_device(c)
+    m = torch.zeros((1, 2), dtype=torch.int8, device="cuda")
+    n = ea.ea_hybrid_prefill_workspace_size(c.B, c.T, max_seqlen(c), c.Hq, c.Hkv, c.d, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(dv["q"], 7.0)
+    note("run over a zeroed (unplanned) workspace")
+    ea.ea_hybrid_prefill_run(dv["q"], dv["k"], dv["v"], m, dv["cu"], max_seqlen(c), ws, out=out,
+                             with_lse=False)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
