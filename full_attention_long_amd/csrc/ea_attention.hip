@@ -51,6 +51,19 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+// bf16 kernel: a row's probabilities may sum to 2^20 before O and l are
+// rescaled (fp32 accumulators and bf16 operands keep their relative precision
+// at any scale; the sum over a whole sequence stays far below float range)
+constexpr float kSumLimit = 1048576.0f;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kValuPerMfma = 8;
+constexpr int kDsAhead = 4;
+constexpr int kPvAhead = 4;
+// word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data, no swizzle)
+constexpr int kBufferWord3 = 0x00020000;
 constexpr float kMinusBig = -1.0e30f;      // finite "minus infinity" for the running max
 
 struct AttnArgs {
@@ -335,9 +348,292 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel.
+//
+// Software pipeline over the item's visible key blocks 0..nblk-1.  Iteration n
+// runs, in one basic block, the score MFMAs of block n + 1 (S = K Q^T) and the
+// PV MFMAs of block n - 1 (O^T += V^T P^T), with the softmax VALU work of
+// block n interleaved between them: exponentials, bf16 conversion, row sums.
+// The exponentials use the running offset m of earlier blocks; only when a
+// row's probabilities sum past 2^kSumLimit (or m is still unset) does a rare
+// branch take the row max, rescale O and l, and recompute P.
+//
+// K and V tiles of 64 keys reach LDS by direct global-to-LDS loads (no
+// register staging), issued one iteration ahead: iteration n loads K_{n+2}
+// into the buffer K_n left free and V_n into the buffer V_{n-2} left free,
+// while it reads K_{n+1} and V_{n-1}.  Each 1 KiB load instruction of a wave
+// fills 4 consecutive (d = 128) rows; rows are unpadded and their 16-byte
+// chunks are XOR-swizzled so that the 16-byte K reads (chunk ^ row % 8) and
+// the transposing V reads (chunk ^ 4 (row % 4)) spread over the LDS banks.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(AttnArgs a) {
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  constexpr int TILE = kBlock * D;               // elements of one K or V tile
+  constexpr int RPI = 1024 / (2 * D);            // rows per 1 KiB load instruction
+  constexpr int NDMA = kBlock / RPI / kAttnWaves;  // load instructions per wave per tile
+  constexpr int DT = D / 32;
+  constexpr int NQ = D / 16;
+  constexpr int KSW = 7;                         // K chunk swizzle: chunk ^ (row & 7)
+  constexpr int VSW = (CPR / 4) - 1;             // V: chunk ^ 4 ((row & 3) & VSW)
+  static_assert(NDMA >= 1 && NDMA * RPI * kAttnWaves == kBlock, "tile must split evenly");
+
+  // four separate LDS arrays, each addressed only through its own name, so that
+  // the compiler can tell a direct load into one from reads of another
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE], Ks1[TILE], Vs0[TILE], Vs1[TILE];
+
+  const int64_t wg = blockIdx.x;
+  const int64_t jx = wg / kNumXcd;
+  const int64_t pos_in_list = ((jx / kXcdChunk) * kNumXcd + (wg % kNumXcd)) * kXcdChunk + (jx % kXcdChunk);
+  if (a.meta[kMetaStamp] != a.stamp) return;  // workspace not planned for these sizes
+  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
+  const Item it = a.items[a.order[pos_in_list]];
+  const int b = it.b, kvh = it.kvh;
+  const int tok0 = a.cu[b];
+  const int L = a.cu[b + 1] - tok0;
+  const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + kvh] != 0 ? 1 : 0;
+  const int ns = a.n_sink;
+  const int w = a.seq_w[b];
+  const int p0 = it.qt * a.BMq;
+  const int p1 = min(p0 + a.BMq, L) - 1;
+  const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
+  int r1_end = 0, r2_beg = 0;
+  if (mode) {
+    const int ws = max(0, qb0 - w + 1);
+    r1_end = min(ns, ws);
+    r2_beg = ws;
+  }
+  const int nblk = r1_end + (qb1 + 1 - r2_beg);
+  auto kb_of = [&](int n) { return n < r1_end ? n : r2_beg + (n - r1_end); };
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, h = lane / 32, lq = lane % 32;
+  const int row = wave * 32 + lq;
+  const int hh = row / a.BMq;
+  const int pos = p0 + row % a.BMq;
+  const bool rvalid = hh < a.G && pos < L;
+  const int hq = kvh * a.G + hh;
+  const int qblk = pos / kBlock;
+
+  bf16x8 qf[NQ];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u)
+      qf[u] = rvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * u + 8 * h) : bf16x8{};
+  }
+
+  // Direct loads of one tile: instruction i of this wave fills rows
+  // r0 .. r0 + RPI - 1 (r0 = (wave NDMA + i) RPI); lane l writes physical chunk
+  // l % CPR of row r0 + l / CPR, i.e. logical chunk (l % CPR) ^ swizzle(row).
+  // The loads go through a buffer resource whose range ends at the sequence
+  // end, so rows past it read as zeros (their probabilities are 0).
+  const int rs = a.Hkv * D;  // row stride; L * rs < 2^31 is checked on the host
+  const uint16_t* Kseq = static_cast<const uint16_t*>(a.K) + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
+  const uint16_t* Vseq = static_cast<const uint16_t*>(a.V) + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
+  int dma_koff[NDMA], dma_voff[NDMA];  // byte offsets within a tile's rows
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = (wave * NDMA + i) * RPI + lane / CPR;
+    dma_koff[i] = (r * rs + ((lane % CPR) ^ (r & KSW)) * 8) * 2;
+    dma_voff[i] = (r * rs + ((lane % CPR) ^ (4 * ((r & 3) & VSW))) * 8) * 2;
+  }
+  auto dma = [&](const uint16_t* seq, const int* off, uint16_t* tile, int kb) {
+    const int key0 = kb * kBlock;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(seq + static_cast<int64_t>(key0) * rs), 0,
+        static_cast<unsigned>(L - key0) * static_cast<unsigned>(rs) * 2u, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(tile + (wave * NDMA + i) * RPI * D), 16,
+          off[i], 0, 0, 0);
+  };
+
+  // Per-lane LDS offsets (elements) of the swizzled reads.
+  // K: row lq (+32), chunk (2u + h) ^ (lq & 7) = 2 (u ^ (lq >> 1 & 3)) + (h ^ lq & 1)
+  // for u < 8 splits into 4 lane offsets plus a uniform 4-chunk step for u >= 4.
+  int koff[4];
+#pragma unroll
+  for (int ul = 0; ul < 4; ++ul) koff[ul] = lq * D + ((2 * ul + h) ^ (lq & KSW)) * 8;
+  // V: rows 16u + 4h + (lane & 15) / 4 (+8), column 32t + 16 ((lane >> 4) & 1) + 4 (lane & 3);
+  // chunk 4t + c_low becomes 4 (t ^ j) + c_low with j = ((lane >> 2) & 3) & VSW.
+  int voff[DT];
+  {
+    const int vr = 4 * h + (lane & 15) / 4;
+    const int clow = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int j = ((lane >> 2) & 3) & VSW;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) voff[t] = vr * D + (4 * (t ^ j) + clow) * 8 + 4 * (lane & 1);
+  }
+
+  auto scores = [&](const uint16_t* kt, f32x16& s0, f32x16& s1) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int o0 = koff[u & 3] + (u >> 2) * 64;
+      s0 = mfma_bf16(*reinterpret_cast<const bf16x8*>(kt + o0), qf[u], s0);
+      s1 = mfma_bf16(*reinterpret_cast<const bf16x8*>(kt + o0 + 32 * D), qf[u], s1);
+    }
+  };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+  float m_run = kMinusBig, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  auto pv = [&](const uint16_t* vt, const bf16x8* pb) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const i16x4 lo = ds_read_tr(vt + voff[t] + 16 * u * D);
+        const i16x4 hi = ds_read_tr(vt + voff[t] + (16 * u + 8) * D);
+        const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, v8), pb[u], o[t]);
+      }
+    }
+    // keep the transposing reads kPvAhead MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + kPvAhead < 4 * DT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+  };
+
+  auto mask = [&](int kb, f32x16& s0, f32x16& s1) {
+    const bool blk_ok = mode == 0 || kb < ns || qblk - kb < w;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
+      if (!(blk_ok && j <= pos)) s0[i] = -INFINITY;
+      if (!(blk_ok && j + 32 <= pos)) s1[i] = -INFINITY;
+    }
+  };
+
+  // P = exp2(s c - m) as bf16 MFMA operands; returns the row sum of the
+  // unrounded values (LSE keeps float32 accuracy).
+  auto expcvt = [&](const f32x16& s0, const f32x16& s1, float nm, bf16x8* pb) {
+    float ls = 0.f;
+    f32x8 t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& sv = q < 2 ? s0 : s1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * (q & 1) + e], c, nm));
+        ls += t[e];
+      }
+      pb[q] = __builtin_convertvector(t, bf16x8);
+    }
+    return ls;
+  };
+
+  // Softmax of one block (scores s0, s1) into pb; rescales O and l when needed.
+  auto softmax = [&](f32x16& s0, f32x16& s1, bf16x8* pb) {
+    float ls = expcvt(s0, s1, -m_run, pb);
+    float row_sum;
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
+      row_sum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // Interleave the next block's score MFMAs (each fed by an LDS read issued
+    // a few MFMAs ahead) with this block's exponentials.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDsAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NQ; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + kDsAhead < 2 * NQ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+    }
+    const bool upd = row_sum > kSumLimit;
+    if (__ballot(upd)) {
+      float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      const float mn = upd ? fmaxf(m_run, mx * c) : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+      bf16x8 pn[4];
+      const float ln = expcvt(s0, s1, -m_run, pn);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pb[u] = upd ? pn[u] : pb[u];
+      ls = upd ? ln : ls;
+    }
+    l_run += ls;
+  };
+
+  // Prologue: K_0, K_1 and V_0 into LDS, scores of block 0.
+  dma(Kseq, dma_koff, Ks0, kb_of(0));
+  dma(Kseq, dma_koff, Ks1, kb_of(min(1, nblk - 1)));
+  dma(Vseq, dma_voff, Vs0, kb_of(0));
+  __syncthreads();
+  f32x16 sa0, sa1, sb0, sb1;
+  scores(Ks0, sa0, sa1);
+  __syncthreads();  // K_0 fully read before K_2 replaces it
+
+  // Iteration n: loads of K_{n+2} (into the K buffer of parity n) and V_{n+1}
+  // (into the V buffer of parity n + 1) in flight; scores of block n + 1 from
+  // the other K buffer interleaved with the softmax of block n; then
+  // O += V_n P_n.  Even and odd iterations are written out separately so that
+  // every LDS array is named statically.
+  auto iter = [&](int n, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1, uint16_t* kload,
+                  const uint16_t* kread, uint16_t* vload, const uint16_t* vread) {
+    const int kb = kb_of(n);
+    const bool full = (kb * kBlock + kBlock - 1 <= p0) && (mode == 0 || kb < ns || qb1 - kb < w);
+    if (!full) mask(kb, c0, c1);
+    dma(Kseq, dma_koff, kload, kb_of(min(n + 2, nblk - 1)));
+    dma(Vseq, dma_voff, vload, kb_of(min(n + 1, nblk - 1)));
+    scores(kread, x0, x1);
+    bf16x8 pb[4];
+    softmax(c0, c1, pb);
+    pv(vread, pb);
+    __syncthreads();
+  };
+  for (int n = 0; n < nblk; n += 2) {
+    iter(n, sa0, sa1, sb0, sb1, Ks0, Ks1, Vs1, Vs0);
+    if (n + 1 < nblk) iter(n + 1, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs1);
+  }
+
+  // Epilogue: O = O^T / l in place in [T, Hq, D]; LSE.
+  float lt;
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    lt = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const float inv = 1.0f / lt;
+  if (rvalid) {
+    uint16_t* orow = static_cast<uint16_t*>(a.O) + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = o[t][4 * q + e] * inv;
+        *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * q + 4 * h) = __builtin_convertvector(v, bf16x4);
+      }
+    }
+    if (h == 0 && a.lse) a.lse[static_cast<int64_t>(hq) * a.T + tok0 + pos] = (m_run + __log2f(lt)) * kLn2;
+  }
+}
+
 template <bool BF16, int D>
 void launch(const AttnArgs& args, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((attention_kernel<BF16, D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+  if constexpr (BF16)
+    hipLaunchKernelGGL((attention_kernel_bf16<D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+  else
+    hipLaunchKernelGGL((attention_kernel<false, D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
 }
 
 }  // namespace

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/ea.h"
+#include "ea.h"
 
 namespace ea {
 
