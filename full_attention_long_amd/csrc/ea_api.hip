@@ -43,10 +43,10 @@ ea_status check_shape(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int3
     return fail(EA_ERR_UNSUPPORTED, "Hq / Hkv must be <= %d (got %d)", ea::kTileRows, G);
   if (d != 64 && d != 128) return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d);
   if (dtype != EA_F32 && dtype != EA_BF16) return fail(EA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
-  // K/V rows of one sequence are addressed with 32-bit element offsets
-  if (static_cast<int64_t>(T > 0 ? max_seqlen : 1) * Hkv * d >= (int64_t(1) << 31))
-    return fail(EA_ERR_UNSUPPORTED, "max_seqlen * Hkv * head_dim must be < 2^31 (got %lld)",
-                (long long)max_seqlen * Hkv * d);
+  // Q, K and V rows of one sequence are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(T > 0 ? max_seqlen : 1) * Hq * d >= (int64_t(1) << 31))
+    return fail(EA_ERR_UNSUPPORTED, "max_seqlen * Hq * head_dim must be < 2^31 (got %lld)",
+                (long long)max_seqlen * Hq * d);
   out->B = B;
   out->T = T;
   out->max_seqlen = T > 0 ? max_seqlen : 1;

@@ -352,20 +352,24 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
 // bf16 kernel.
 //
 // Software pipeline over the item's visible key blocks 0..nblk-1.  Iteration n
-// runs, in one basic block, the score MFMAs of block n + 1 (S = K Q^T) and the
-// PV MFMAs of block n - 1 (O^T += V^T P^T), with the softmax VALU work of
-// block n interleaved between them: exponentials, bf16 conversion, row sums.
-// The exponentials use the running offset m of earlier blocks; only when a
-// row's probabilities sum past 2^kSumLimit (or m is still unset) does a rare
-// branch take the row max, rescale O and l, and recompute P.
+// computes, in one basic block, the score MFMAs of block n + 1 (S = K Q^T)
+// with the softmax VALU work of block n interleaved between them
+// (exponentials, bf16 conversion, row sums), then O^T += V_n^T P_n^T.  The
+// exponentials use the row's running offset m of earlier blocks; only when a
+// row's probabilities sum past kSumLimit (or m is unset) does a rare branch
+// take the row max, rescale O and l, and recompute P.
 //
-// K and V tiles of 64 keys reach LDS by direct global-to-LDS loads (no
-// register staging), issued one iteration ahead: iteration n loads K_{n+2}
-// into the buffer K_n left free and V_n into the buffer V_{n-2} left free,
-// while it reads K_{n+1} and V_{n-1}.  Each 1 KiB load instruction of a wave
-// fills 4 consecutive (d = 128) rows; rows are unpadded and their 16-byte
-// chunks are XOR-swizzled so that the 16-byte K reads (chunk ^ row % 8) and
-// the transposing V reads (chunk ^ 4 (row % 4)) spread over the LDS banks.
+// K and V tiles of 64 keys reach LDS by direct buffer-to-LDS loads (no
+// register staging) one iteration ahead: iteration n loads K_{n+2} into the
+// buffer K_n left free and V_{n+1} into the buffer V_{n-1} left free, while it
+// reads K_{n+1} and V_n.  Each 1 KiB load instruction of a wave fills 4
+// (d = 128) or 8 (d = 64) consecutive rows.  V rows are unpadded with their
+// 16-byte chunks XOR-swizzled by 4 (row % 4) for the transposing reads; K rows
+// form groups of one load instruction, the groups padded by 64 bytes and the
+// chunks within a group XOR-swizzled, so that the 16-byte K reads of 16
+// consecutive rows hit 16 distinct bank groups.  (Both layouts read with no
+// LDS bank conflicts.)  The buffer range ends at the sequence end, so rows
+// past it read as zeros.  LDS operand reads run a few MFMAs ahead of their use.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(AttnArgs a) {
@@ -375,13 +379,17 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   constexpr int NDMA = kBlock / RPI / kAttnWaves;  // load instructions per wave per tile
   constexpr int DT = D / 32;
   constexpr int NQ = D / 16;
-  constexpr int KSW = 7;                         // K chunk swizzle: chunk ^ (row & 7)
+  // K tile: groups of RPI rows (one load instruction each) padded by 64 bytes;
+  // within a group, row j's chunks are XOR-swizzled by kfold(j) in 0..3.
+  constexpr int KGS = RPI * D + 32;              // K group stride (elements)
+  constexpr int KTILE = (kBlock / RPI) * KGS;    // elements of one K tile
   constexpr int VSW = (CPR / 4) - 1;             // V: chunk ^ 4 ((row & 3) & VSW)
   static_assert(NDMA >= 1 && NDMA * RPI * kAttnWaves == kBlock, "tile must split evenly");
+  auto kfold = [](int j) { return D == 128 ? j : (j >> 1); };
 
   // four separate LDS arrays, each addressed only through its own name, so that
   // the compiler can tell a direct load into one from reads of another
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE], Ks1[TILE], Vs0[TILE], Vs1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KTILE], Ks1[KTILE], Vs0[TILE], Vs1[TILE];
 
   const int64_t wg = blockIdx.x;
   const int64_t jx = wg / kNumXcd;
@@ -427,8 +435,6 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   // Direct loads of one tile: instruction i of this wave fills rows
   // r0 .. r0 + RPI - 1 (r0 = (wave NDMA + i) RPI); lane l writes physical chunk
   // l % CPR of row r0 + l / CPR, i.e. logical chunk (l % CPR) ^ swizzle(row).
-  // The loads go through a buffer resource whose range ends at the sequence
-  // end, so rows past it read as zeros (their probabilities are 0).
   const int rs = a.Hkv * D;  // row stride; L * rs < 2^31 is checked on the host
   const uint16_t* Kseq = static_cast<const uint16_t*>(a.K) + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
   const uint16_t* Vseq = static_cast<const uint16_t*>(a.V) + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
@@ -436,10 +442,10 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int r = (wave * NDMA + i) * RPI + lane / CPR;
-    dma_koff[i] = (r * rs + ((lane % CPR) ^ (r & KSW)) * 8) * 2;
+    dma_koff[i] = (r * rs + ((lane % CPR) ^ kfold(lane / CPR)) * 8) * 2;
     dma_voff[i] = (r * rs + ((lane % CPR) ^ (4 * ((r & 3) & VSW))) * 8) * 2;
   }
-  auto dma = [&](const uint16_t* seq, const int* off, uint16_t* tile, int kb) {
+  auto dma = [&](const uint16_t* seq, const int* off, uint16_t* tile, int gstride, int kb) {
     const int key0 = kb * kBlock;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(seq + static_cast<int64_t>(key0) * rs), 0,
@@ -447,16 +453,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(tile + (wave * NDMA + i) * RPI * D), 16,
+          rsrc, (__attribute__((address_space(3))) void*)(tile + (wave * NDMA + i) * gstride), 16,
           off[i], 0, 0, 0);
   };
 
   // Per-lane LDS offsets (elements) of the swizzled reads.
-  // K: row lq (+32), chunk (2u + h) ^ (lq & 7) = 2 (u ^ (lq >> 1 & 3)) + (h ^ lq & 1)
-  // for u < 8 splits into 4 lane offsets plus a uniform 4-chunk step for u >= 4.
-  int koff[4];
-#pragma unroll
-  for (int ul = 0; ul < 4; ++ul) koff[ul] = lq * D + ((2 * ul + h) ^ (lq & KSW)) * 8;
+  // K: row lq (+32), in group g = lq / RPI at j = lq % RPI, chunk
+  // (2u + h) ^ f = 2 (u ^ b) + (h ^ e) with f = kfold(j) = 2b + e: an even-u
+  // and an odd-u lane offset plus a uniform 16u.  Over any 16 consecutive rows
+  // the 16-byte reads of one chunk land on 16 distinct bank groups.
+  int koff_e, koff_o;
+  {
+    const int j = lq % RPI, f = kfold(j), bb = f >> 1, e = f & 1;
+    const int base = (lq / RPI) * KGS + j * D + (h ^ e) * 8;
+    koff_e = base + 16 * bb;
+    koff_o = base - 16 * bb;
+  }
   // V: rows 16u + 4h + (lane & 15) / 4 (+8), column 32t + 16 ((lane >> 4) & 1) + 4 (lane & 3);
   // chunk 4t + c_low becomes 4 (t ^ j) + c_low with j = ((lane >> 2) & 3) & VSW.
   int voff[DT];
@@ -473,9 +485,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     s1 = f32x16{};
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int o0 = koff[u & 3] + (u >> 2) * 64;
+      const int o0 = ((u & 1) ? koff_o : koff_e) + 16 * u;
       s0 = mfma_bf16(*reinterpret_cast<const bf16x8*>(kt + o0), qf[u], s0);
-      s1 = mfma_bf16(*reinterpret_cast<const bf16x8*>(kt + o0 + 32 * D), qf[u], s1);
+      s1 = mfma_bf16(*reinterpret_cast<const bf16x8*>(kt + o0 + (32 / RPI) * KGS), qf[u], s1);
     }
   };
 
@@ -573,9 +585,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   };
 
   // Prologue: K_0, K_1 and V_0 into LDS, scores of block 0.
-  dma(Kseq, dma_koff, Ks0, kb_of(0));
-  dma(Kseq, dma_koff, Ks1, kb_of(min(1, nblk - 1)));
-  dma(Vseq, dma_voff, Vs0, kb_of(0));
+  dma(Kseq, dma_koff, Ks0, KGS, kb_of(0));
+  dma(Kseq, dma_koff, Ks1, KGS, kb_of(min(1, nblk - 1)));
+  dma(Vseq, dma_voff, Vs0, RPI * D, kb_of(0));
   __syncthreads();
   f32x16 sa0, sa1, sb0, sb1;
   scores(Ks0, sa0, sa1);
@@ -591,8 +603,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     const int kb = kb_of(n);
     const bool full = (kb * kBlock + kBlock - 1 <= p0) && (mode == 0 || kb < ns || qb1 - kb < w);
     if (!full) mask(kb, c0, c1);
-    dma(Kseq, dma_koff, kload, kb_of(min(n + 2, nblk - 1)));
-    dma(Vseq, dma_voff, vload, kb_of(min(n + 1, nblk - 1)));
+    dma(Kseq, dma_koff, kload, KGS, kb_of(min(n + 2, nblk - 1)));
+    dma(Vseq, dma_voff, vload, RPI * D, kb_of(min(n + 1, nblk - 1)));
     scores(kread, x0, x1);
     bf16x8 pb[4];
     softmax(c0, c1, pb);

@@ -148,9 +148,9 @@ size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t
  *               (256-byte aligned); not shared between concurrent calls
  *
  * head_dim must be 64 or 128; Hq must be a multiple of Hkv with
- * Hq / Hkv <= 256; max_seqlen * Hkv * head_dim must be < 2^31 (one
- * sequence's K or V addressed with 32-bit element offsets: 2M tokens at
- * Hkv = 8, d = 128).  Each output row is written by exactly one workgroup with
+ * Hq / Hkv <= 256; max_seqlen * Hq * head_dim must be < 2^31 (one
+ * sequence's rows are addressed with 32-bit byte offsets: 512K tokens at
+ * Hq = 32, d = 128).  Each output row is written by exactly one workgroup with
  * no atomics on O, so results are bitwise reproducible. */
 ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
                             const int8_t* modes, const int32_t* cu_seqlens, int32_t B,

@@ -69,7 +69,7 @@ def _prefill(**kw):
     (dict(max_seqlen=0), -1, "max_seqlen"),
     (dict(max_seqlen=2000), -1, "max_seqlen"),
     (dict(T=2**31), -1, "total_tokens"),
-    (dict(T=2**30, max_seqlen=2**21, Hq=64, Hkv=8), -2, "2^31"),
+    (dict(T=2**30, max_seqlen=2**20, Hq=32, Hkv=8), -2, "2^31"),
     (dict(ws=None), -3, "workspace"),
     (dict(ws_bytes=1024), -3, "workspace"),
     (dict(ws=FAKE + 16), -1, "256-byte"),
