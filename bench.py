@@ -39,7 +39,10 @@ if ROOT not in sys.path:
 
 METRIC = "hybrid prefill effective TFLOP/s + ms/layer at 128K; % bf16 MFMA roofline"
 DEFAULT_RUNS = ["qwen4b_s128k_sa2", "qwen4b_s128k_sa6"]
-ATTN_SRC = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attention.hip")
+# The sources that decide the attention kernel's memory traffic: the kernel and
+# the work-list order that places its workgroups on the XCDs.
+ATTN_SRCS = [os.path.join(ROOT, "full_attention_long_amd", "csrc", f)
+             for f in ("ea_attention.hip", "ea_worklist.hip", "ea_internal.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attention_traffic.json")
 ATTN_KERNEL = "attention_kernel"
 CALIB_KERNEL = "bitwise_not"
@@ -50,8 +53,11 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in ATTN_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class Layer:
@@ -315,7 +321,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": "attention_kernel<bf16, 128>",
+            "kernel": "ea::attention_kernel_bf16<128>",
             "avg_launch_ms": round(attn_sum / len(runs), 4),
             "flops_per_launch": round(tot_ef / len(runs), 0),
         },

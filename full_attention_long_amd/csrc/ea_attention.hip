@@ -363,13 +363,13 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
 // register staging) one iteration ahead: iteration n loads K_{n+2} into the
 // buffer K_n left free and V_{n+1} into the buffer V_{n-1} left free, while it
 // reads K_{n+1} and V_n.  Each 1 KiB load instruction of a wave fills 4
-// (d = 128) or 8 (d = 64) consecutive rows.  V rows are unpadded with their
-// 16-byte chunks XOR-swizzled by 4 (row % 4) for the transposing reads; K rows
-// form groups of one load instruction, the groups padded by 64 bytes and the
-// chunks within a group XOR-swizzled, so that the 16-byte K reads of 16
-// consecutive rows hit 16 distinct bank groups.  (Both layouts read with no
-// LDS bank conflicts.)  The buffer range ends at the sequence end, so rows
-// past it read as zeros.  LDS operand reads run a few MFMAs ahead of their use.
+// (d = 128) or 8 (d = 64) consecutive rows.  K rows sit in groups of one
+// instruction's rows, each group padded by 64 bytes, with the 16-byte chunks
+// of a row XOR-swizzled inside its group; V rows are unpadded with chunks
+// swizzled by 4 (row % 4).  Both spread the 16-byte K reads and the
+// transposing V reads over the 64 LDS banks.  The buffer range ends at the
+// sequence end, so rows past it read as zeros.  LDS operand reads run a few
+// MFMAs ahead of their use.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(AttnArgs a) {

@@ -13,9 +13,15 @@ namespace ea {
 // 32 rows per wave of the attention kernel's workgroup.
 constexpr int kTileRows = 256;
 constexpr int kAttnWaves = kTileRows / 32;
-// Consecutive work-list entries given to one XCD before moving to the next.
-constexpr int kXcdChunk = 8;
+// Consecutive work-list entries given to one XCD before moving to the next:
+// one entry per CU of the XCD, so the workgroups that run together on an XCD
+// take neighbouring entries (same KV head, adjacent query tiles) and share
+// their K/V rows in that XCD's L2.
+constexpr int kXcdChunk = 32;
 constexpr int kNumXcd = 8;
+// The work list is ordered by cost in bands of 2^kCostBandShift key blocks,
+// so that entries within a band keep their head / sequence / tile order.
+constexpr int kCostBandShift = 5;
 // Key/value block of the sparse pattern and of the attention inner loop.
 constexpr int kBlock = 64;
 

@@ -107,9 +107,15 @@ __device__ __forceinline__ int item_cost(int mode, int p0, int p1, int n_sink, i
   return min(n_sink, ws) + (qb1 + 1 - ws);
 }
 
-// Raw item x (KV head major, then sequence, then query tile), its sort key
-// (bin 0 = most expensive; nbins for the unused slots past the item count)
-// and its index as the sort value.
+// Sort key of a cost: 0 for the most expensive band of 2^kCostBandShift
+// blocks; max_key(nbins) for the unused slots past the item count.
+__host__ __device__ __forceinline__ uint32_t max_key(int32_t nbins) {
+  return static_cast<uint32_t>(((nbins - 1) >> kCostBandShift) + 1);
+}
+
+// Raw item x (KV head major, then sequence, then query tile from the last,
+// most expensive tile down), its banded sort key and its index as the sort
+// value; the stable sort keeps this raw order inside a band.
 __global__ __launch_bounds__(256) void items_kernel(
     const int32_t* __restrict__ cu, const int8_t* __restrict__ modes, int32_t B, int32_t Hkv,
     int32_t BMq, int32_t n_sink, const int32_t* __restrict__ meta,
@@ -121,13 +127,13 @@ __global__ __launch_bounds__(256) void items_kernel(
   vals[x] = static_cast<int32_t>(x);
   const int32_t tiles = meta[kMetaTiles];
   if (x >= static_cast<int64_t>(tiles) * Hkv) {
-    keys[x] = static_cast<uint32_t>(nbins);
+    keys[x] = max_key(nbins);
     return;
   }
   const int kvh = static_cast<int>(x / tiles);
   const int32_t rem = static_cast<int32_t>(x - static_cast<int64_t>(kvh) * tiles);
   const int b = find_seq(tile_prefix, B, rem);
-  const int qt = rem - tile_prefix[b];
+  const int qt = (tile_prefix[b + 1] - 1) - rem;
   const int L = cu[b + 1] - cu[b];
   const int p0 = qt * BMq, p1 = min(p0 + BMq, L) - 1;
   const int mode = modes[static_cast<int64_t>(b) * Hkv + kvh] != 0 ? 1 : 0;
@@ -138,12 +144,12 @@ __global__ __launch_bounds__(256) void items_kernel(
   it.qt = qt;
   it.cost = cost;
   raw[x] = it;
-  keys[x] = static_cast<uint32_t>(nbins - 1 - min(cost, nbins - 1));
+  keys[x] = static_cast<uint32_t>((nbins - 1 - min(cost, nbins - 1)) >> kCostBandShift);
 }
 
-int key_bits(int32_t nbins) {
+int key_bits(uint32_t max_value) {
   int bits = 1;
-  while ((int64_t(1) << bits) <= nbins) ++bits;
+  while ((int64_t(1) << bits) <= max_value) ++bits;
   return bits;
 }
 
@@ -158,7 +164,7 @@ Workspace plan_workspace(const Shape& s) {
   hipError_t e = hipcub::DeviceRadixSort::SortPairs(
       nullptr, sort_tmp, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
       static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
-      static_cast<int>(w.max_items), 0, key_bits(w.nbins), static_cast<hipStream_t>(nullptr));
+      static_cast<int>(w.max_items), 0, key_bits(max_key(w.nbins)), static_cast<hipStream_t>(nullptr));
   if (e != hipSuccess) sort_tmp = 0;
   size_t off = 0;
   w.meta = off;        off = align(off + sizeof(int32_t) * kMetaSlots);
@@ -196,7 +202,7 @@ hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* mode
   size_t tmp_bytes = ws.sort_tmp_bytes;
   return hipcub::DeviceRadixSort::SortPairs(base + ws.sort_tmp, tmp_bytes, keys_in, keys_out,
                                             vals_in, order, static_cast<int>(ws.max_items), 0,
-                                            key_bits(ws.nbins), st);
+                                            key_bits(max_key(ws.nbins)), st);
 }
 
 }  // namespace ea
