@@ -18,21 +18,21 @@
 // V^T operand is read from the row-major V tile with gfx950's transposing LDS
 // read (ds_read_b64_tr_b16), whose 4-key groups also match the key order the
 // MFMA result leaves in each lane.  K and V blocks of 64 keys are
-// double-buffered through LDS: the next block's coalesced 16-byte global loads
-// are issued before the current block's MFMAs and land in the other buffer
-// after them, one barrier per block.
+// double-buffered through LDS, the next blocks' loads in flight during the
+// current block's MFMAs, one barrier per block.
 //
 // Work-list entries are mapped onto the XCDs in chunks: the hardware hands
 // workgroup i to XCD i mod 8, and workgroup i takes list entry
-// ((j / C) * 8 + i mod 8) * C + j mod C with j = i / 8, C = 8.  The workgroups
-// resident on one XCD then hold runs of consecutive entries, which the sort
-// keeps in query order within a KV head, so they stream the same K/V blocks
-// through that XCD's L2 at about the same time.
+// ((j / C) * 8 + i mod 8) * C + j mod C with j = i / 8 and C = kXcdChunk (one
+// entry per CU of an XCD).  The workgroups resident on one XCD then hold runs
+// of consecutive entries, which the banded cost sort keeps in query-tile order
+// within a KV head, so they stream the same K/V blocks through that XCD's L2 at
+// about the same time.
 //
 // Online softmax in base 2 (scale * log2 e folded into one FMA per score) with
-// a lazy rescale: the running max only moves, and O and l are only rescaled,
-// when a row's block max exceeds it by more than 8 (probabilities stay <= 2^8,
-// the ratio O / l is unchanged).
+// a lazy running max: the float32 kernel moves it, and rescales O and l, only
+// when a row's block max exceeds it by more than 8; the bf16 kernel only when
+// a row's probabilities sum past 2^20.  Either way the ratio O / l is exact.
 #include "ea_internal.h"
 
 #include <type_traits>
