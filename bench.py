@@ -16,7 +16,10 @@ against the MI355X dense bf16 MFMA peak.  `traffic` is that kernel's HBM bytes
 per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by what the
 same counters read for an elementwise kernel of known size), read from
 profiles/attention_traffic.json when it was taken on the current kernel
-source, else null.
+source, else null.  `mfma_loop_tflops` is the practical ceiling beside the
+data-sheet peak: the library's MFMA-loop probe (8 waves per CU issuing
+back-to-back bf16 MFMAs with no memory traffic) at whatever clock the board
+holds under that load, measured in the same run.
 
 Prints one JSON line.  --gpus must be 1: the path is measured on one GPU.
 """
@@ -50,6 +53,37 @@ CALIB_KERNEL = "bitwise_not"
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def mfma_probe(target_ms: float = 100.0, launches: int = 3) -> dict:
+    """Practical bf16 matrix-core ceiling: the library's MFMA-loop probe (one
+    workgroup of 8 waves per CU, back-to-back 32x32x16 bf16 MFMAs, no memory
+    traffic) timed with HIP events on the current stream."""
+    import torch
+
+    import full_attention_long_amd as ea
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(n * 512, dtype=torch.float32, device="cuda")
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(iters):
+        a, b = E(), E()
+        a.record()
+        flops = ea.ea_mfma_probe(out, n, iters)
+        b.record()
+        torch.cuda.synchronize()
+        return flops, a.elapsed_time(b)
+
+    timed(2000)
+    _, ms = timed(20000)
+    iters = max(1000, int(20000 * target_ms / max(ms, 1e-3)))
+    timed(iters)  # settle the clock under the full-length load
+    res = [timed(iters) for _ in range(launches)]
+    ms = float(np.median([r[1] for r in res]))
+    flops = res[0][0]
+    assert bool(torch.isfinite(out).all()), "probe checksums not finite"
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3),
+            "workgroups": n, "iters": iters}
 
 
 def kernel_source_hash() -> str:
@@ -215,7 +249,7 @@ def summarize_counters(pmc_dirs, calib_mib, layers_flops, out_path):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--runs", default=",".join(DEFAULT_RUNS),
                     help="comma-separated workload names; one step runs each once")
@@ -280,6 +314,7 @@ def main():
         seg = np.array([[evs[s][li][k].elapsed_time(evs[s][li][k + 1]) for k in range(3)]
                         for s in range(args.steps)])
         route_ms, plan_ms, attn_ms = seg.mean(axis=0)
+        attn_med = float(np.median(seg[:, 2]))
         layer_ms = float(seg.sum(axis=1).mean())
         m = ly.modes.cpu().numpy()
         runs.append({
@@ -289,12 +324,16 @@ def main():
             "effective_flops": int(efs[li]), "ms_per_layer": round(layer_ms, 4),
             "route_ms": round(float(route_ms), 4), "plan_ms": round(float(plan_ms), 4),
             "attention_ms": round(float(attn_ms), 4),
+            "attention_ms_median": round(attn_med, 4),
             "effective_tflops": round(efs[li] / (layer_ms * 1e-3) / 1e12, 3),
             "attention_tflops": round(efs[li] / (attn_ms * 1e-3) / 1e12, 3),
             "seed": c.seed,
         })
         log(f"{ly.name}: layer {layer_ms:.3f} ms (route {route_ms:.3f}, plan {plan_ms:.3f}, "
             f"attention {attn_ms:.3f}) -> {runs[-1]['effective_tflops']:.1f} TFLOP/s")
+    log("matrix-core ceiling probe")
+    probe = mfma_probe()
+    log(f"probe: {probe['tflops']:.1f} TFLOP/s ({probe['ms']:.1f} ms per launch)")
     tot_ef = float(sum(efs))
     value = tot_ef / (step_ms * 1e-3) / 1e12
     attn_sum = sum(r["attention_ms"] for r in runs)
@@ -324,6 +363,10 @@ def main():
             "kernel": "ea::attention_kernel_bf16<128>",
             "avg_launch_ms": round(attn_sum / len(runs), 4),
             "flops_per_launch": round(tot_ef / len(runs), 0),
+            "traffic_gbps": (round(traffic / (attn_sum / len(runs) * 1e-3) / 1e9, 1)
+                             if traffic is not None else None),
+            "mfma_loop_tflops": probe["tflops"],
+            "frac_of_mfma_loop": round(achieved / probe["tflops"], 4),
         },
     }
     if not args.no_cpu_baseline:

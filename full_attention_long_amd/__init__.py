@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     ea_hybrid_prefill_run,
     ea_hybrid_prefill_workspace_size,
     ea_last_error,
+    ea_mfma_probe,
     ea_route,
     header_functions,
     lib,

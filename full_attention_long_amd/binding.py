@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.ea_hybrid_prefill_run.restype = i32
     L.ea_hybrid_prefill_run.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                         ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
+    L.ea_mfma_probe.restype = i32
+    L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
     return L
 
@@ -211,3 +213,16 @@ def ea_hybrid_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace
                                        ctypes.byref(sp), _ptr(out), _ptr(lse), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def ea_mfma_probe(out, n_workgroups: int, iters: int, *, seed: int = 1, stream=None) -> int:
+    """Launch the matrix-core ceiling probe into ``out`` (float32 device tensor
+    of n_workgroups * 512 elements); returns the FLOPs the launch performs."""
+    _dev(out, "out")
+    import torch
+    if out.dtype != torch.float32 or out.numel() < n_workgroups * 512:
+        raise ValueError("out must be float32 with at least n_workgroups * 512 elements")
+    flops = ctypes.c_int64(0)
+    _check(lib().ea_mfma_probe(_ptr(out), n_workgroups, iters, seed & 0xFFFFFFFF,
+                               ctypes.byref(flops), _stream(stream)))
+    return flops.value

@@ -195,4 +195,18 @@ ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtyp
   return ok();
 }
 
+ea_status ea_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,
+                        int64_t* flops, void* stream) {
+  if (!out) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (n_workgroups < 1 || n_workgroups > (1 << 20))
+    return fail(EA_ERR_INVALID_ARG, "n_workgroups must be in [1, 2^20] (got %d)", n_workgroups);
+  if (iters < 1 || iters > (1 << 26))
+    return fail(EA_ERR_INVALID_ARG, "iters must be in [1, 2^26] (got %d)", iters);
+  if (!aligned16(out)) return fail(EA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (flops) *flops = ea::mfma_probe_flops(n_workgroups, iters);
+  hipError_t e = ea::launch_mfma_probe(out, n_workgroups, iters, seed, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -21,11 +21,10 @@
 // double-buffered through LDS, the next blocks' loads in flight during the
 // current block's MFMAs, one barrier per block.
 //
-// Work-list entries are mapped onto the XCDs in chunks: the hardware hands
-// workgroup i to XCD i mod 8, and workgroup i takes list entry
-// ((j / C) * 8 + i mod 8) * C + j mod C with j = i / 8 and C = kXcdChunk (one
-// entry per CU of an XCD).  The workgroups resident on one XCD then hold runs
-// of consecutive entries, which the banded cost sort keeps in query-tile order
+// Work-list entries are mapped onto the XCDs in chunks of C = kXcdChunk
+// consecutive entries (one per CU of an XCD), dealt to the 8 XCDs in snake
+// order (list_position).  The workgroups resident on one XCD then hold runs of
+// consecutive entries, which the banded cost sort keeps in query-tile order
 // within a KV head, so they stream the same K/V blocks through that XCD's L2 at
 // about the same time.
 //
@@ -83,6 +82,17 @@ struct AttnArgs {
   float scale_log2;
 };
 
+// Work-list position of workgroup wg.  The hardware hands workgroup wg to XCD
+// wg mod 8; the j-th workgroup an XCD receives (j = wg / 8) takes entry
+// j mod C of chunk 8 (j / C) + x of the list, C = kXcdChunk, with x = wg mod 8
+// in even rounds j / C and 7 - wg mod 8 in odd ones.  Chunks are cost-sorted,
+// so the snake keeps any XCD from taking the costlier chunk of every round.
+__device__ __forceinline__ int64_t list_position(int64_t wg) {
+  const int64_t j = wg / kNumXcd, round = j / kXcdChunk;
+  const int64_t x = (round & 1) ? (kNumXcd - 1 - wg % kNumXcd) : (wg % kNumXcd);
+  return (round * kNumXcd + x) * kXcdChunk + j % kXcdChunk;
+}
+
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -121,9 +131,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
   __shared__ __attribute__((aligned(16))) E Vs[2][kBlock * VROW];
 
   // XCD-chunked position in the cost-sorted work list
-  const int64_t wg = blockIdx.x;
-  const int64_t jx = wg / kNumXcd;
-  const int64_t pos_in_list = ((jx / kXcdChunk) * kNumXcd + (wg % kNumXcd)) * kXcdChunk + (jx % kXcdChunk);
+  const int64_t pos_in_list = list_position(blockIdx.x);
   if (a.meta[kMetaStamp] != a.stamp) return;  // workspace not planned for these sizes
   if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
   const Item it = a.items[a.order[pos_in_list]];
@@ -391,9 +399,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   // the compiler can tell a direct load into one from reads of another
   __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KTILE], Ks1[KTILE], Vs0[TILE], Vs1[TILE];
 
-  const int64_t wg = blockIdx.x;
-  const int64_t jx = wg / kNumXcd;
-  const int64_t pos_in_list = ((jx / kXcdChunk) * kNumXcd + (wg % kNumXcd)) * kXcdChunk + (jx % kXcdChunk);
+  const int64_t pos_in_list = list_position(blockIdx.x);
   if (a.meta[kMetaStamp] != a.stamp) return;  // workspace not planned for these sizes
   if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
   const Item it = a.items[a.order[pos_in_list]];

@@ -91,4 +91,9 @@ hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, co
                             const void* V, const int8_t* modes, const int32_t* cu, void* O,
                             float* lse, const Workspace& ws, char* base, hipStream_t st);
 
+// Matrix-core ceiling probe (ea_probe.hip) and its FLOP count.
+hipError_t launch_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,
+                             hipStream_t st);
+int64_t mfma_probe_flops(int32_t n_workgroups, int32_t iters);
+
 }  // namespace ea

@@ -188,6 +188,25 @@ ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_
                                 float* lse, const void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* ea_mfma_probe - measurement helper, not part of the attention path: the
+ * practical bf16 matrix-core ceiling that the attention kernel's throughput is
+ * set against beside the data-sheet peak (256 CUs x 2.4 GHz x 4096 FLOP/clk).
+ *
+ * Launches n_workgroups workgroups of 8 waves (one per CU: each reserves
+ * 96 KiB of LDS), each wave issuing `iters` rounds of 16 back-to-back
+ * v_mfma_f32_32x32x16_bf16 over 4 independent accumulators, operands random
+ * bf16 drawn from `seed` and held in registers: no memory traffic in the loop,
+ * so the board's clock settles where a pure matrix load puts it.
+ *
+ *   out     out float32 [n_workgroups * 512] device buffer (16-byte aligned),
+ *           one checksum per thread (keeps the loop live; values not meaningful)
+ *   flops   out, host: FLOPs the launch performs
+ *           (n_workgroups * 8 * iters * 16 * 32768), or NULL
+ *
+ * 1 <= n_workgroups <= 2^20, 1 <= iters <= 2^26.  Asynchronous on `stream`. */
+ea_status ea_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,
+                        int64_t* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

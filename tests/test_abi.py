@@ -16,7 +16,7 @@ def test_every_header_function_is_exported():
     names = ea.header_functions()
     assert set(names) == {"ea_abi_version", "ea_last_error", "ea_route",
                           "ea_hybrid_prefill_workspace_size", "ea_hybrid_prefill",
-                          "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run"}
+                          "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run", "ea_mfma_probe"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -139,3 +139,20 @@ def test_plan_and_run_host_errors():
     # zero tokens: nothing to do
     assert L.ea_hybrid_prefill_plan(FAKE, FAKE, 1, 0, 0, 8, 2, 128, 1, ctypes.byref(sp),
                                     FAKE, 1 << 40, None) == 0
+
+
+def test_mfma_probe_host_errors():
+    L = ea.lib()
+    flops = ctypes.c_int64(0)
+    cases = [
+        (dict(out=None, n=256, iters=10), "null pointer"),
+        (dict(out=FAKE, n=0, iters=10), "n_workgroups"),
+        (dict(out=FAKE, n=2**20 + 1, iters=10), "n_workgroups"),
+        (dict(out=FAKE, n=256, iters=0), "iters"),
+        (dict(out=FAKE, n=256, iters=2**26 + 1), "iters"),
+        (dict(out=FAKE + 4, n=256, iters=10), "aligned"),
+    ]
+    for c, msg in cases:
+        st = L.ea_mfma_probe(c["out"], c["n"], c["iters"], 1, ctypes.byref(flops), None)
+        assert st == bnd.EA_ERR_INVALID_ARG, (c, st)
+        assert msg in ea.ea_last_error(), (c, ea.ea_last_error())
