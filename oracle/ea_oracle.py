@@ -16,6 +16,13 @@ What is computed, and where the pages define it:
 * Hard routing r_hard = argmax over the two columns, 0 = FA, 1 = SA (router
   paragraph on Fig. 3(b) and the Gumbel-Softmax paragraph: inference uses
   hard decisions).
+* Training-time routing: r_soft = Gumbel-Softmax of z (softmax over the two
+  modes of (z + g) / tau, g standard Gumbel noise, tau the annealed
+  temperature), r_hard = argmax of r_soft, and the straight-through estimator
+  r = r_hard - sg(r_soft) + r_soft whose forward value is r_hard (the
+  Gumbel-Softmax and STE paragraphs of the method section; "Technical
+  Summary: Elastic Attention", Sec. 2.2).  The training forward computes each
+  head in both modes and mixes the two outputs with r (dual-mode forward).
 * Per KV head either full causal attention (FA equation of the preliminaries)
   or sparse attention over a retained subset of K/V (SA equation); query heads
   share their group's K/V and mode (GQA footnote of the hybrid-head equation);
@@ -248,6 +255,95 @@ def attention_weights(Q, K, modes, L, hq, *, G, block=64, n_sink=1, window_block
     _, _, P = _attend(Q[:L, hq], np.arange(L), K[:L, g], Vdummy, int(modes[0, g]), ns, w, block,
                       _scale(d, softmax_scale), return_weights=True)
     return P
+
+
+# ----------------------------------------------------------------------------
+# Training forward: Gumbel-Softmax routing with straight-through hard decisions,
+# and the dual-mode attention it mixes
+# ----------------------------------------------------------------------------
+
+
+def gumbel_route(z, g, tau: float):
+    """Routing of the training forward for logits z [..., 2] and noise g [..., 2].
+
+    y = (z + g) / tau, taken in float32 as the library takes it, so that the
+    hard decision is made in one precision on both sides; r_soft = softmax(y)
+    over the last axis (float64 from the float32 y); r_hard = argmax of r_soft,
+    which is the argmax of y (softmax is monotone), a tie going to FA (index 0).
+    Returns (r_soft float64 [..., 2], modes int8 [...])."""
+    z32 = np.asarray(z, dtype=np.float32)
+    g32 = np.zeros_like(z32) if g is None else np.asarray(g, dtype=np.float32)
+    y = (z32 + g32) / np.float32(tau)
+    y64 = y.astype(np.float64)
+    e = np.exp(y64 - y64.max(axis=-1, keepdims=True))
+    r_soft = e / e.sum(axis=-1, keepdims=True)
+    modes = (y[..., 1] > y[..., 0]).astype(np.int8)
+    return r_soft, modes
+
+
+def ste_weights(r_soft, modes):
+    """Straight-through mixing weights r = r_hard - sg(r_soft) + r_soft, as
+    their forward values (the stop-gradient is the identity in a forward
+    pass), float64 [..., 2]; r_hard is the one-hot of ``modes``."""
+    r_hard = np.stack([1 - np.asarray(modes), np.asarray(modes)], axis=-1).astype(np.float64)
+    return r_hard - r_soft + r_soft
+
+
+def dual_attention(Q, K, V, cu_seqlens, r_soft, modes, *, block=64, n_sink=1, window_blocks=0,
+                   keep_fraction=0.2, softmax_scale=0.0):
+    """Dual-mode training forward of one layer: every query head in both modes.
+
+    O_FA = the FA output of every head, O_SA = the SA output of every head (the
+    FA and SA equations, all heads), and the layer output mixes them per
+    (sequence, KV head) with the straight-through weights of ``r_soft`` and
+    ``modes``: O = r[0] O_FA + r[1] O_SA.  Returns (O, O_FA, O_SA, LSE_FA,
+    LSE_SA), float64, O's [T, Hq, d] and LSE's [Hq, T]."""
+    B = len(cu_seqlens) - 1
+    Hkv = K.shape[1]
+    geom = dict(block=block, n_sink=n_sink, window_blocks=window_blocks,
+                keep_fraction=keep_fraction, softmax_scale=softmax_scale)
+    O_fa, L_fa = hybrid_attention(Q, K, V, np.zeros((B, Hkv), np.int8), cu_seqlens, **geom)
+    O_sa, L_sa = hybrid_attention(Q, K, V, np.ones((B, Hkv), np.int8), cu_seqlens, **geom)
+    O = _mix(O_fa, O_sa, cu_seqlens, ste_weights(r_soft, modes))
+    return O, O_fa, O_sa, L_fa, L_sa
+
+
+def _mix(O_fa, O_sa, cu_seqlens, r):
+    T, Hq, _ = O_fa.shape
+    G = Hq // r.shape[1]
+    O = np.zeros_like(O_fa)
+    for b in range(len(cu_seqlens) - 1):
+        s0, e0 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        for hq in range(Hq):
+            rb = r[b, hq // G]
+            O[s0:e0, hq] = rb[0] * O_fa[s0:e0, hq] + rb[1] * O_sa[s0:e0, hq]
+    return O
+
+
+def dual_attention_rows(Q, K, V, cu_seqlens, r_soft, modes, tokens, heads, *, block=64, n_sink=1,
+                        window_blocks=0, keep_fraction=0.2, softmax_scale=0.0):
+    """dual_attention at selected global token indices and query heads only.
+
+    Returns (O, O_FA, O_SA) float64 [len(tokens), len(heads), d] and (LSE_FA,
+    LSE_SA) float64 [len(tokens), len(heads)]."""
+    B = len(cu_seqlens) - 1
+    Hkv = K.shape[1]
+    G = Q.shape[1] // Hkv
+    geom = dict(block=block, n_sink=n_sink, window_blocks=window_blocks,
+                keep_fraction=keep_fraction, softmax_scale=softmax_scale)
+    O_fa, L_fa = hybrid_attention_rows(Q, K, V, np.zeros((B, Hkv), np.int8), cu_seqlens, tokens,
+                                       heads, **geom)
+    O_sa, L_sa = hybrid_attention_rows(Q, K, V, np.ones((B, Hkv), np.int8), cu_seqlens, tokens,
+                                       heads, **geom)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    seg = np.searchsorted(np.asarray(cu_seqlens, np.int64), tokens, side="right") - 1
+    r = ste_weights(r_soft, modes)
+    O = np.zeros_like(O_fa)
+    for ti, b in enumerate(seg):
+        for hi, hq in enumerate(heads):
+            rb = r[b, hq // G]
+            O[ti, hi] = rb[0] * O_fa[ti, hi] + rb[1] * O_sa[ti, hi]
+    return O, O_fa, O_sa, L_fa, L_sa
 
 
 # ----------------------------------------------------------------------------

@@ -1,0 +1,145 @@
+"""Pins of the oracle's training forward (Gumbel-Softmax routing with
+straight-through hard decisions, and the dual-mode attention it mixes) against
+closed forms, the Gumbel-max property, textbook attention and invariants."""
+import math
+
+import numpy as np
+import torch
+
+from oracle import ea_oracle as orc
+from workloads import gen
+
+
+def _rand(seed, *shape, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ----------------------------------------------------------------------------
+# Gumbel-Softmax routing
+# ----------------------------------------------------------------------------
+
+def test_gumbel_route_exact_values():
+    # softmax((0, ln 3) / 1) = (1/4, 3/4); the same at tau = 2 with doubled logits
+    r, m = orc.gumbel_route(np.array([[0.0, math.log(3.0)]]), None, 1.0)
+    np.testing.assert_allclose(r, [[0.25, 0.75]], atol=1e-7)
+    assert m.tolist() == [1]
+    r, m = orc.gumbel_route(np.array([[0.0, 2 * math.log(3.0)]]), None, 2.0)
+    np.testing.assert_allclose(r, [[0.25, 0.75]], atol=1e-7)
+    # (ln 3, 0) reversed: FA wins
+    r, m = orc.gumbel_route(np.array([[math.log(3.0), 0.0]]), None, 1.0)
+    np.testing.assert_allclose(r, [[0.75, 0.25]], atol=1e-7)
+    assert m.tolist() == [0]
+
+
+def test_gumbel_route_is_logistic_of_the_noisy_margin():
+    # two classes: softmax(y)[1] = 1 / (1 + exp(y0 - y1)), y = (z + g) / tau
+    z, g = _rand(1, 50, 2, scale=2.0), _rand(2, 50, 2)
+    for tau in (0.3, 1.0, 4.0):
+        r, m = orc.gumbel_route(z, g, tau)
+        y = (z.astype(np.float32) + g.astype(np.float32)) / np.float32(tau)
+        want = 1.0 / (1.0 + np.exp(y[:, 0].astype(np.float64) - y[:, 1].astype(np.float64)))
+        np.testing.assert_allclose(r[:, 1], want, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r.sum(-1), 1.0, atol=1e-15)
+        assert np.array_equal(m, (r[:, 1] > r[:, 0]).astype(np.int8))
+
+
+def test_gumbel_route_tie_goes_to_fa_and_low_temperature_is_one_hot():
+    r, m = orc.gumbel_route(np.array([[1.5, 1.5], [-2.0, -2.0]]), None, 0.7)
+    assert m.tolist() == [0, 0]
+    np.testing.assert_allclose(r, 0.5, atol=0)
+    z, g = _rand(3, 40, 2), _rand(4, 40, 2)
+    r, m = orc.gumbel_route(z, g, 1e-3)
+    hard = np.stack([1 - m, m], -1)
+    keep = np.abs((z + g)[:, 1] - (z + g)[:, 0]) > 0.05   # margins well above tau
+    np.testing.assert_allclose(r[keep], hard[keep], atol=1e-12)
+
+
+def test_gumbel_noise_statistics_and_gumbel_max_property():
+    g = gen.draw_gumbel(5, (400000, 2)).astype(np.float64)
+    # standard Gumbel: mean = Euler-Mascheroni gamma, variance = pi^2 / 6
+    assert abs(g.mean() - 0.5772156649) < 0.005
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.01
+    # argmax(z + g) is distributed as softmax(z): the hard decisions of the
+    # Gumbel-Softmax router sample SA with probability sigmoid(z1 - z0)
+    z = np.tile(np.array([[0.3, 1.1]]), (g.shape[0], 1))
+    _, m = orc.gumbel_route(z, g, 1.0)
+    p = 1.0 / (1.0 + math.exp(0.3 - 1.1))
+    assert abs(m.mean() - p) < 4 * math.sqrt(p * (1 - p) / len(m))
+
+
+def test_ste_forward_value_is_the_hard_decision():
+    z, g = _rand(6, 64, 2), _rand(7, 64, 2)
+    r_soft, m = orc.gumbel_route(z, g, 0.5)
+    r = orc.ste_weights(r_soft, m)
+    np.testing.assert_allclose(r, np.stack([1 - m, m], -1), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# Dual-mode attention
+# ----------------------------------------------------------------------------
+
+def _sdpa(Q, K, V):
+    q = torch.from_numpy(Q).permute(1, 0, 2)[None]
+    k = torch.from_numpy(K).permute(1, 0, 2)[None]
+    v = torch.from_numpy(V).permute(1, 0, 2)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _case(seed, lengths, Hq, Hkv, d):
+    T = int(sum(lengths))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    Q, K, V = _rand(seed, T, Hq, d), _rand(seed + 1, T, Hkv, d), _rand(seed + 2, T, Hkv, d)
+    z, g = _rand(seed + 3, len(lengths), Hkv, 2), _rand(seed + 4, len(lengths), Hkv, 2)
+    r_soft, m = orc.gumbel_route(z, g, 1.0)
+    return Q, K, V, cu, r_soft, m
+
+
+def test_dual_fa_output_is_causal_sdpa_and_sa_is_blockwise_for_a_one_block_window():
+    Q, K, V, cu, r_soft, m = _case(10, [333], 8, 2, 16)
+    O, O_fa, O_sa, L_fa, L_sa = orc.dual_attention(Q, K, V, cu, r_soft, m, n_sink=0,
+                                                   window_blocks=1)
+    np.testing.assert_allclose(O_fa, _sdpa(Q, K, V), rtol=0, atol=1e-12)
+    for s in range(0, 333, 64):
+        e = min(333, s + 64)
+        np.testing.assert_allclose(O_sa[s:e], _sdpa(Q[s:e], K[s:e], V[s:e]), rtol=0, atol=1e-12)
+
+
+def test_dual_lse_superset_and_covering_window():
+    Q, K, V, cu, r_soft, m = _case(20, [700, 90], 4, 2, 8)
+    _, O_fa, O_sa, L_fa, L_sa = orc.dual_attention(Q, K, V, cu, r_soft, m, n_sink=1,
+                                                   window_blocks=2)
+    # FA sees a superset of SA's keys: its log-sum-exp is never smaller
+    assert (L_fa >= L_sa - 1e-12).all()
+    # rows whose causal keys all lie in sinks + window: both modes agree
+    np.testing.assert_allclose(O_sa[:192], O_fa[:192], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(O_sa[700:790], O_fa[700:790], rtol=0, atol=1e-13)
+    assert np.abs(O_sa[192:700] - O_fa[192:700]).max() > 1e-3
+    # and the merge identity the fused kernel relies on: the FA sum of
+    # exponentials is the SA one plus that of the keys SA leaves out
+    assert (np.exp(L_fa[:, 192:700]) > np.exp(L_sa[:, 192:700]) * (1 + 1e-9)).all()
+
+
+def test_dual_mix_selects_by_hard_decision_per_kv_group():
+    Q, K, V, cu, _, _ = _case(30, [150, 260], 8, 4, 8)
+    m = np.array([[0, 1, 1, 0], [1, 0, 0, 1]], np.int8)
+    r_soft = np.full((2, 4, 2), 0.5)
+    O, O_fa, O_sa, _, _ = orc.dual_attention(Q, K, V, cu, r_soft, m, n_sink=1, window_blocks=1)
+    G = 2
+    for b in range(2):
+        s0, e0 = cu[b], cu[b + 1]
+        for hq in range(8):
+            want = O_sa if m[b, hq // G] else O_fa
+            np.testing.assert_allclose(O[s0:e0, hq], want[s0:e0, hq], rtol=0, atol=1e-15)
+
+
+def test_dual_rows_api_equals_full():
+    Q, K, V, cu, r_soft, m = _case(40, [200, 130], 8, 2, 8)
+    full = orc.dual_attention(Q, K, V, cu, r_soft, m, n_sink=1, window_blocks=1)
+    toks = np.array([0, 5, 63, 64, 199, 200, 201, 329])
+    heads = [0, 3, 7]
+    rows = orc.dual_attention_rows(Q, K, V, cu, r_soft, m, toks, heads, n_sink=1, window_blocks=1)
+    for k in range(3):
+        np.testing.assert_allclose(rows[k], full[k][toks][:, heads], rtol=0, atol=1e-14)
+    for k in range(3, 5):
+        np.testing.assert_allclose(rows[k], full[k][heads][:, toks].T, rtol=0, atol=1e-14)

@@ -27,7 +27,7 @@ from .configs import Workload
 STREAM = {
     "q": 1, "k": 2, "v": 3, "lowrank_a": 4, "lowrank_b": 5,
     "w1": 6, "b1": 7, "w2": 8, "b2": 9, "w3": 10, "b3": 11, "w4": 12, "b4": 13,
-    "lengths": 14, "heads": 15,
+    "lengths": 14, "heads": 15, "gumbel": 16,
 }
 CHUNK_ROWS = 4096
 CONTROL_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "route_control.json")
@@ -116,6 +116,12 @@ def draw_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     """Sequence lengths floor(exp(U(ln lo, ln hi))), int64."""
     u = _rng(seed, STREAM["lengths"]).uniform(np.log(lo), np.log(hi), size=n)
     return np.floor(np.exp(u)).astype(np.int64)
+
+
+def draw_gumbel(seed: int, shape) -> np.ndarray:
+    """Standard Gumbel(0, 1) noise, float32, from its own stream (the noise the
+    Gumbel-Softmax router draws during training, passed in as an input)."""
+    return _rng(seed, STREAM["gumbel"]).gumbel(0.0, 1.0, size=tuple(shape)).astype(np.float32)
 
 
 def draw_sa_heads(seed: int, counts, Hkv: int):
