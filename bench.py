@@ -197,6 +197,121 @@ def cpu_baseline(cases, budget_s=12.0):
     }
 
 
+def cpu_baseline_dual(c, budget_s=12.0):
+    """The oracle's dual-mode forward on a bounded sample of the layer: 64-row
+    query blocks of one query head at seeded positions, each computed in both
+    modes, until ~budget_s of CPU time is spent; the FA FLOPs of the sample
+    (the dual forward's effective work) over its wall time."""
+    from oracle import ea_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    qf, kf, vf = c.q_f32(), c.k_f32(), c.v_f32()
+    L = int(c.lengths[0])
+    r_soft = np.full((c.B, c.Hkv, 2), 0.5)
+    modes = np.zeros((c.B, c.Hkv), np.int8)
+    done_flops, units, t_used = 0, 0, 0.0
+    while t_used < budget_s and units < 512:
+        hq = units % c.Hq
+        qb = int(rng.integers(0, L // 64))
+        toks = np.arange(qb * 64, min(L, qb * 64 + 64))
+        t0 = time.perf_counter()
+        orc.dual_attention_rows(qf, kf, vf, c.cu_seqlens, r_soft, modes, toks, [hq],
+                                n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+        t_used += time.perf_counter() - t0
+        done_flops += 4 * c.d * len(toks) * 64 * (qb + 1)
+        units += 1
+    return {
+        "value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{units} query blocks of 64 rows x one query head at seeded positions of "
+                  f"{c.name}, each in both modes; float64 two-pass softmax; {t_used:.1f} s of "
+                  f"CPU; {platform.machine()} host",
+    }
+
+
+def bench_dual(args):
+    """Dual-mode (training) forward of one layer: router logits, Gumbel-Softmax
+    hard decisions, and the dual attention (work list, one attention launch
+    over every head's SA set and the rest of its causal blocks, merge); prints
+    one JSON line of its own."""
+    import torch
+
+    import full_attention_long_amd as ea
+    from full_attention_long_amd import metrics
+    from workloads import gen
+    name = args.runs.split(",")[0]
+    ly = Layer(name)
+    c = ly.case
+    noise = torch.from_numpy(gen.draw_gumbel(c.seed, (c.B, c.Hkv, 2))).cuda()
+    r_soft = torch.empty((c.B, c.Hkv, 2), dtype=torch.float32, device="cuda")
+    O_fa, O_sa = torch.empty_like(ly.q), torch.empty_like(ly.q)
+    lse_fa = torch.empty((c.Hq, c.T), dtype=torch.float32, device="cuda")
+    lse_sa = torch.empty_like(lse_fa)
+    nbytes = ea.ea_dual_prefill_workspace_size(c.B, c.T, ly.maxlen, c.Hq, c.Hkv, c.d, 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ea.ea_route(ly.k, ly.cu, ly.w, pool_len=c.pool_len, modes=ly.modes, logits=ly.logits)
+        ea.ea_gumbel_route(ly.logits, args.tau, gumbel=noise, r_soft=r_soft, modes=ly.modes)
+        if ev is not None:
+            ev[1].record()
+        ea.ea_dual_prefill(ly.q, ly.k, ly.v, ly.cu, ly.maxlen, modes=ly.modes, out=ly.O,
+                           out_fa=O_fa, out_sa=O_sa, lse_fa=lse_fa, lse_sa=lse_sa, workspace=ws,
+                           **ly.geom)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ef = metrics.effective_flops(np.zeros((c.B, c.Hkv), np.int8), c.lengths, c.Hq, c.Hkv, c.d,
+                                 n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[E() for _ in range(3)] for _ in range(args.steps)]
+    start, stop = E(), E()
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / args.steps
+    seg = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])
+    route_ms, dual_ms = seg.mean(axis=0)
+    log(f"dual {name}: step {step_ms:.3f} ms (routing {route_ms:.3f}, dual forward {dual_ms:.3f})")
+    probe = mfma_probe()
+    achieved = ef / (dual_ms * 1e-3) / 1e12
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
+    out = {
+        "metric": "dual-mode training forward effective TFLOP/s at 128K (FA FLOPs of every head)",
+        "value": round(ef / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name + ":dual", "seq_len": ly.maxlen, "Hq": c.Hq, "Hkv": c.Hkv,
+                   "d": c.d, "tau": args.tau, "effective_flops": int(ef),
+                   "routing_ms": round(float(route_ms), 4),
+                   "dual_forward_ms": round(float(dual_ms), 4),
+                   "sa_kv_heads": int(ly.modes.sum().item())},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "ea_dual_prefill (work list + ea::attention_kernel_bf16<128> + "
+                               "dual_merge_kernel)",
+                     "mfma_loop_tflops": probe["tflops"],
+                     "frac_of_mfma_loop": round(achieved / probe["tflops"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_dual(c, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def calibrate(mib):
     """One elementwise kernel of known traffic (reads and writes mib MiB), so
     that profiler byte counters can be scaled to bytes."""
@@ -255,6 +370,10 @@ def main():
                     help="comma-separated workload names; one step runs each once")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--dual", action="store_true",
+                    help="measure the dual-mode (training) forward of the first --runs workload "
+                         "instead (default qwen4b_s128k_sa6)")
+    ap.add_argument("--tau", type=float, default=1.0, help="Gumbel-Softmax temperature (--dual)")
     ap.add_argument("--calibrate-mib", type=int, default=0,
                     help="first run one elementwise kernel that reads and writes this many MiB "
                          "(for scaling profiler byte counters)")
@@ -278,6 +397,11 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_mib:
         calibrate(args.calibrate_mib)
+    if args.dual:
+        if args.runs == ",".join(DEFAULT_RUNS):
+            args.runs = "qwen4b_s128k_sa6"
+        bench_dual(args)
+        return
     layers = [Layer(n) for n in args.runs.split(",")]
 
     log(f"warmup {args.warmup} steps")

@@ -7,6 +7,9 @@ throughput.
 from .binding import (  # noqa: F401
     EAError,
     ea_abi_version,
+    ea_dual_prefill,
+    ea_dual_prefill_workspace_size,
+    ea_gumbel_route,
     ea_hybrid_prefill,
     ea_hybrid_prefill_plan,
     ea_hybrid_prefill_run,

@@ -74,6 +74,13 @@ def lib() -> ctypes.CDLL:
     L.ea_hybrid_prefill_run.restype = i32
     L.ea_hybrid_prefill_run.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                         ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
+    L.ea_gumbel_route.restype = i32
+    L.ea_gumbel_route.argtypes = [vp, vp, ctypes.c_float, i32, vp, vp, vp]
+    L.ea_dual_prefill_workspace_size.restype = sz
+    L.ea_dual_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.ea_dual_prefill.restype = i32
+    L.ea_dual_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                  ctypes.POINTER(SparsityParams), vp, vp, vp, vp, vp, vp, sz, vp]
     L.ea_mfma_probe.restype = i32
     L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
@@ -213,6 +220,69 @@ def ea_hybrid_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace
                                        ctypes.byref(sp), _ptr(out), _ptr(lse), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def ea_gumbel_route(logits, tau: float, *, gumbel=None, r_soft=None, modes=None,
+                    with_soft: bool = True, stream=None):
+    """Training-time routing of float32 logits [..., 2]: r_soft = softmax((logits +
+    gumbel) / tau) and the hard modes (int8 [...], 1 = SA) of the straight-through
+    estimator."""
+    import torch
+    _dev(logits, "logits")
+    if logits.dtype != torch.float32 or logits.shape[-1] != 2:
+        raise ValueError("logits must be float32 [..., 2]")
+    if gumbel is not None:
+        _dev(gumbel, "gumbel")
+        if gumbel.shape != logits.shape or gumbel.dtype != torch.float32:
+            raise ValueError("gumbel must be float32 of the logits' shape")
+    n = logits.numel() // 2
+    if modes is None:
+        modes = torch.empty(logits.shape[:-1], dtype=torch.int8, device=logits.device)
+    if r_soft is None and with_soft:
+        r_soft = torch.empty_like(logits)
+    _check(lib().ea_gumbel_route(_ptr(logits), _ptr(gumbel), float(tau), n, _ptr(r_soft),
+                                 _ptr(modes), _stream(stream)))
+    return r_soft, modes
+
+
+def ea_dual_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype_code):
+    return int(lib().ea_dual_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv,
+                                                    head_dim, dtype_code))
+
+
+def ea_dual_prefill(Q, K, V, cu_seqlens, max_seqlen: int, *, modes=None, n_sink: int = 1,
+                    window_blocks: int = 0, keep_fraction: float = 0.2, softmax_scale: float = 0.0,
+                    block: int = 64, out=None, out_fa=None, out_sa=None, lse_fa=None, lse_sa=None,
+                    workspace=None, stream=None):
+    """Dual-mode (training) forward: every head in both modes.
+
+    Returns (O, O_FA, O_SA, LSE_FA, LSE_SA); O (the straight-through mix, the
+    hard decision's output per (sequence, KV head)) only when ``modes`` is
+    given, else None."""
+    import torch
+    for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (cu_seqlens, "cu_seqlens")]:
+        _dev(t, n)
+    if modes is not None:
+        _dev(modes, "modes")
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    B = cu_seqlens.numel() - 1
+    code = _dtype_code(Q)
+    if out is None and modes is not None:
+        out = torch.empty_like(Q)
+    out_fa = torch.empty_like(Q) if out_fa is None else out_fa
+    out_sa = torch.empty_like(Q) if out_sa is None else out_sa
+    lse_fa = torch.empty((Hq, T), dtype=torch.float32, device=Q.device) if lse_fa is None else lse_fa
+    lse_sa = torch.empty((Hq, T), dtype=torch.float32, device=Q.device) if lse_sa is None else lse_sa
+    if workspace is None:
+        need = ea_dual_prefill_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    _check(lib().ea_dual_prefill(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes), _ptr(cu_seqlens),
+                                 B, T, max_seqlen, Hq, Hkv, d, ctypes.byref(sp), _ptr(out),
+                                 _ptr(out_fa), _ptr(out_sa), _ptr(lse_fa), _ptr(lse_sa),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, out_fa, out_sa, lse_fa, lse_sa
 
 
 def ea_mfma_probe(out, n_workgroups: int, iters: int, *, seed: int = 1, stream=None) -> int:

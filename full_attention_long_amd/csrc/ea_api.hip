@@ -60,12 +60,14 @@ ea_status check_shape(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int3
 }
 
 // Shared validation of the plan, run and one-shot prefill calls.
+// parts: 1 for the routed forward (modes required), 2 for the dual-mode one.
 ea_status check_prefill(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
                         int32_t d, ea_dtype dtype, const ea_sparsity_params* p, const void* modes,
                         const void* cu_seqlens, const void* workspace, size_t workspace_bytes,
-                        ea::Shape* s, ea::Workspace* ws, ea::Geometry* g) {
+                        ea::Shape* s, ea::Workspace* ws, ea::Geometry* g, int parts = 1) {
   ea_status st = check_shape(B, T, max_seqlen, Hq, Hkv, d, dtype, s);
   if (st != EA_OK) return st;
+  s->parts = parts;
   if (!p) return fail(EA_ERR_INVALID_ARG, "null sparsity params");
   if (p->block != ea::kBlock)
     return fail(EA_ERR_UNSUPPORTED, "sparsity block must be %d (got %d)", ea::kBlock, p->block);
@@ -75,7 +77,7 @@ ea_status check_prefill(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, in
     return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1] (got %g)", (double)p->keep_fraction);
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
     return fail(EA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (!modes || !cu_seqlens) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if ((parts == 1 && !modes) || !cu_seqlens) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
   *ws = ea::plan_workspace(*s);
   if (!workspace || workspace_bytes < ws->total)
     return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", ws->total,
@@ -167,8 +169,8 @@ ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_
   if (st != EA_OK) return st;
   if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
   if (total_tokens == 0) return ok();
-  hipError_t e = ea::launch_attention(s, g, Q, K, V, modes, cu_seqlens, O, lse, ws,
-                                      static_cast<char*>(const_cast<void*>(workspace)),
+  hipError_t e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr},
+                                      ws, static_cast<char*>(const_cast<void*>(workspace)),
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(EA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -190,8 +192,61 @@ ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtyp
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
-  if (e == hipSuccess) e = ea::launch_attention(s, g, Q, K, V, modes, cu_seqlens, O, lse, ws, base, hs);
+  if (e == hipSuccess)
+    e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr}, ws,
+                             base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ea_status ea_gumbel_route(const float* logits, const float* gumbel, float tau, int32_t n,
+                          float* r_soft, int8_t* modes, void* stream) {
+  if (!logits || !modes) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (n < 0) return fail(EA_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
+  if (!(tau > 0.f) || isinf(tau)) return fail(EA_ERR_INVALID_ARG, "tau must be finite and > 0");
+  hipError_t e = ea::launch_gumbel_route(logits, gumbel, tau, n, r_soft, modes,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t ea_dual_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                      int32_t Hq, int32_t Hkv, int32_t head_dim, ea_dtype dtype) {
+  ea::Shape s;
+  if (check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s) != EA_OK) return 0;
+  g_err.clear();
+  s.parts = 2;
+  return ea::plan_workspace(s).total;
+}
+
+ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                          const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                          int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                          int32_t head_dim, const ea_sparsity_params* p, void* O, void* O_fa,
+                          void* O_sa, float* lse_fa, float* lse_sa, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  ea_status st = check_prefill(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, modes,
+                               cu_seqlens, workspace, workspace_bytes, &s, &ws, &g, 2);
+  if (st != EA_OK) return st;
+  if ((st = check_tensors(Q, K, V, O_fa)) != EA_OK) return st;
+  if (!O_sa || !lse_fa || !lse_sa) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(O_sa) || (O && !aligned16(O)))
+    return fail(EA_ERR_INVALID_ARG, "O, O_fa and O_sa must be 16-byte aligned");
+  if (O && !modes) return fail(EA_ERR_INVALID_ARG, "modes is required when O is requested");
+  if (O_fa == O_sa || (O && (O == O_fa || O == O_sa)) || lse_fa == lse_sa)
+    return fail(EA_ERR_INVALID_ARG, "the outputs must not alias");
+  if (total_tokens == 0) return ok();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e == hipSuccess)
+    e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O_sa, lse_sa, O_fa, lse_fa},
+                             ws, base, hs);
+  if (e == hipSuccess) e = ea::launch_dual_merge(s, cu_seqlens, modes, O_sa, lse_sa, O_fa, lse_fa, O, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "dual prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

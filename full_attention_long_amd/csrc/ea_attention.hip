@@ -69,16 +69,17 @@ struct AttnArgs {
   const void* Q;
   const void* K;
   const void* V;
-  void* O;
+  void* O;          // outputs of FA and SA items
   float* lse;
-  const int8_t* modes;
+  void* O_mid;      // outputs of middle-set items (dual-mode forward)
+  float* lse_mid;
   const int32_t* cu;
   const int32_t* seq_w;
   const Item* items;
   const int32_t* order;
   const int32_t* meta;
   int64_t T;
-  int32_t Hq, Hkv, G, BMq, n_sink, stamp;
+  int32_t Hq, Hkv, G, BMq, n_sink, stamp, parts;
   float scale_log2;
 };
 
@@ -91,6 +92,21 @@ __device__ __forceinline__ int64_t list_position(int64_t wg) {
   const int64_t j = wg / kNumXcd, round = j / kXcdChunk;
   const int64_t x = (round & 1) ? (kNumXcd - 1 - wg % kNumXcd) : (wg % kNumXcd);
   return (round * kNumXcd + x) * kXcdChunk + j % kXcdChunk;
+}
+
+// Whether every row of a tile over query positions [p0, ...] (query blocks
+// [qb0, qb1]) sees every key of block kb, so that the block needs no mask.
+__device__ __forceinline__ bool block_full(int mode, int kb, int p0, int qb0, int qb1, int ns, int w) {
+  if (mode == kModeMiddle) return qb0 - kb >= w;
+  return (kb * kBlock + kBlock - 1 <= p0) && (mode == kModeFA || kb < ns || qb1 - kb < w);
+}
+
+// Whether a row in query block qblk may see block kb at all (the causal test
+// on single keys is applied on top; in the middle set it always holds, since
+// kb <= qblk - w < qblk).
+__device__ __forceinline__ bool block_visible(int mode, int kb, int qblk, int ns, int w) {
+  if (mode == kModeMiddle) return qblk - kb >= w;
+  return mode == kModeFA || kb < ns || qblk - kb < w;
 }
 
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -133,26 +149,24 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
   // XCD-chunked position in the cost-sorted work list
   const int64_t pos_in_list = list_position(blockIdx.x);
   if (a.meta[kMetaStamp] != a.stamp) return;  // workspace not planned for these sizes
-  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
+  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv * a.parts) return;
   const Item it = a.items[a.order[pos_in_list]];
   const int b = it.b, kvh = it.kvh;
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + kvh] != 0 ? 1 : 0;
+  const int mode = it.mode;
   const int ns = a.n_sink;
   const int w = a.seq_w[b];
   const int p0 = it.qt * a.BMq;
   const int p1 = min(p0 + a.BMq, L) - 1;
   const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
 
-  // Visible key blocks: FA [0, qb1]; SA sinks [0, r1_end) then window [r2_beg, qb1].
-  int r1_end = 0, r2_beg = 0;
-  if (mode) {
-    const int ws = max(0, qb0 - w + 1);
-    r1_end = min(ns, ws);
-    r2_beg = ws;
-  }
-  const int nblk = r1_end + (qb1 + 1 - r2_beg);
+  // Visible key blocks: [0, r1_end) then [r2_beg, r2_beg + nblk - r1_end).
+  const KeyRange kr = key_range(mode, qb0, qb1, ns, w);
+  const int r1_end = kr.r1_end, r2_beg = kr.r2_beg;
+  const int nblk = kr.count();
+  E* const Oout = static_cast<E*>(mode == kModeMiddle ? a.O_mid : a.O);
+  float* const lse_out = mode == kModeMiddle ? a.lse_mid : a.lse;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h = lane / 32, lq = lane % 32;
@@ -253,9 +267,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
     }
 
     // ---- mask the diagonal and window-edge blocks (element (i) is key 8(i/4)+4h+(i%4)) ----
-    const bool full = (kb * kBlock + kBlock - 1 <= p0) && (mode == 0 || kb < ns || qb1 - kb < w);
+    const bool full = block_full(mode, kb, p0, qb0, qb1, ns, w);
     if (!full) {
-      const bool blk_ok = mode == 0 || kb < ns || qblk - kb < w;
+      const bool blk_ok = block_visible(mode, kb, qblk, ns, w);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
@@ -329,10 +343,11 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
   }
 
   // ---- epilogue: O = O^T / l, written in place in [T, Hq, D]; LSE ----
+  // (a row that sees no key of a middle-set item gets O = 0 and LSE = -inf)
   const float lt = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / lt;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (rvalid) {
-    E* orow = static_cast<E*>(a.O) + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+    E* orow = Oout + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
 #pragma unroll
@@ -352,7 +367,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
         }
       }
     }
-    if (h == 0 && a.lse) a.lse[static_cast<int64_t>(hq) * a.T + tok0 + pos] = (m_run + __log2f(lt)) * kLn2;
+    if (h == 0 && lse_out)
+      lse_out[static_cast<int64_t>(hq) * a.T + tok0 + pos] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -401,25 +417,24 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
 
   const int64_t pos_in_list = list_position(blockIdx.x);
   if (a.meta[kMetaStamp] != a.stamp) return;  // workspace not planned for these sizes
-  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
+  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv * a.parts) return;
   const Item it = a.items[a.order[pos_in_list]];
   const int b = it.b, kvh = it.kvh;
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + kvh] != 0 ? 1 : 0;
+  const int mode = it.mode;
   const int ns = a.n_sink;
   const int w = a.seq_w[b];
   const int p0 = it.qt * a.BMq;
   const int p1 = min(p0 + a.BMq, L) - 1;
   const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
-  int r1_end = 0, r2_beg = 0;
-  if (mode) {
-    const int ws = max(0, qb0 - w + 1);
-    r1_end = min(ns, ws);
-    r2_beg = ws;
-  }
-  const int nblk = r1_end + (qb1 + 1 - r2_beg);
+  const KeyRange kr = key_range(mode, qb0, qb1, ns, w);
+  const int r1_end = kr.r1_end, r2_beg = kr.r2_beg;
+  const int nblk = kr.count();
   auto kb_of = [&](int n) { return n < r1_end ? n : r2_beg + (n - r1_end); };
+  uint16_t* const Oout = static_cast<uint16_t*>(mode == kModeMiddle ? a.O_mid : a.O);
+  float* const lse_out = mode == kModeMiddle ? a.lse_mid : a.lse;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h = lane / 32, lq = lane % 32;
@@ -524,7 +539,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   };
 
   auto mask = [&](int kb, f32x16& s0, f32x16& s1) {
-    const bool blk_ok = mode == 0 || kb < ns || qblk - kb < w;
+    const bool blk_ok = block_visible(mode, kb, qblk, ns, w);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
@@ -590,6 +605,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     l_run += ls;
   };
 
+  // A middle-set tile can have no block at all (its rows see no key beyond the
+  // SA set): it skips straight to the epilogue and writes O = 0, LSE = -inf.
+  if (nblk > 0) {
   // Prologue: K_0, K_1 and V_0 into LDS, scores of block 0.
   dma(Kseq, dma_koff, Ks0, KGS, kb_of(0));
   dma(Kseq, dma_koff, Ks1, KGS, kb_of(min(1, nblk - 1)));
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   auto iter = [&](int n, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1, uint16_t* kload,
                   const uint16_t* kread, uint16_t* vload, const uint16_t* vread) {
     const int kb = kb_of(n);
-    const bool full = (kb * kBlock + kBlock - 1 <= p0) && (mode == 0 || kb < ns || qb1 - kb < w);
+    const bool full = block_full(mode, kb, p0, qb0, qb1, ns, w);
     if (!full) mask(kb, c0, c1);
     dma(Kseq, dma_koff, kload, KGS, kb_of(min(n + 2, nblk - 1)));
     dma(Vseq, dma_voff, vload, RPI * D, kb_of(min(n + 1, nblk - 1)));
@@ -621,6 +639,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     iter(n, sa0, sa1, sb0, sb1, Ks0, Ks1, Vs1, Vs0);
     if (n + 1 < nblk) iter(n + 1, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs1);
   }
+  }
 
   // Epilogue: O = O^T / l in place in [T, Hq, D]; LSE.
   float lt;
@@ -628,10 +647,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
     lt = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  const float inv = 1.0f / lt;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;  // no visible key (middle set): O = 0
   if (rvalid) {
-    uint16_t* orow = static_cast<uint16_t*>(a.O) + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    uint16_t* orow = Oout + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
 #pragma unroll
@@ -642,7 +660,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
         *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * q + 4 * h) = __builtin_convertvector(v, bf16x4);
       }
     }
-    if (h == 0 && a.lse) a.lse[static_cast<int64_t>(hq) * a.T + tok0 + pos] = (m_run + __log2f(lt)) * kLn2;
+    if (h == 0 && lse_out)
+      lse_out[static_cast<int64_t>(hq) * a.T + tok0 + pos] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -657,15 +676,16 @@ void launch(const AttnArgs& args, unsigned grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
-                            const void* V, const int8_t* modes, const int32_t* cu, void* O,
-                            float* lse, const Workspace& ws, char* base, hipStream_t st) {
+                            const void* V, const int32_t* cu, const AttnOut& out,
+                            const Workspace& ws, char* base, hipStream_t st) {
   AttnArgs a;
   a.Q = Q;
   a.K = K;
   a.V = V;
-  a.O = O;
-  a.lse = lse;
-  a.modes = modes;
+  a.O = out.O;
+  a.lse = out.lse;
+  a.O_mid = out.O_mid;
+  a.lse_mid = out.lse_mid;
   a.cu = cu;
   a.seq_w = reinterpret_cast<const int32_t*>(base + ws.seq_w);
   a.items = reinterpret_cast<const Item*>(base + ws.items_raw);
@@ -678,6 +698,7 @@ hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, co
   a.BMq = s.BMq;
   a.n_sink = g.n_sink;
   a.stamp = plan_stamp(s);
+  a.parts = s.parts;
   a.scale_log2 = g.scale_log2;
   constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
   const unsigned grid = static_cast<unsigned>((ws.max_items + span - 1) / span * span);

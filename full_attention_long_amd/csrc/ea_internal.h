@@ -25,13 +25,44 @@ constexpr int kCostBandShift = 5;
 // Key/value block of the sparse pattern and of the attention inner loop.
 constexpr int kBlock = 64;
 
-// One attention work item: a query tile of one KV-head group of one sequence.
+// Key-block sets an attention work item can cover.
+enum ItemMode : int32_t {
+  kModeFA = 0,      // every causal key block
+  kModeSA = 1,      // sink blocks and the local window
+  kModeMiddle = 2   // the causal blocks SA leaves out: FA = SA set + middle set
+};
+
+// One attention work item: a query tile of one KV-head group of one sequence,
+// over one key-block set.
 struct Item {
   int32_t b;     // sequence
   int32_t kvh;   // KV head
   int32_t qt;    // query tile: positions [qt * BMq, qt * BMq + BMq)
   int32_t cost;  // visible key blocks (scheduling key)
+  int32_t mode;  // ItemMode
 };
+
+// Key blocks a query tile covering query blocks [qb0, qb1] visits in `mode`,
+// in order: [0, r1_end) then [r2_beg, kend).  SA: the sinks below the first
+// row's window, then the union of the rows' windows; middle: the blocks from
+// the last sink to the last row's window start, exclusive.
+struct KeyRange {
+  int r1_end, r2_beg, kend;
+  __host__ __device__ int count() const { return r1_end + (kend > r2_beg ? kend - r2_beg : 0); }
+};
+
+__host__ __device__ inline KeyRange key_range(int mode, int qb0, int qb1, int n_sink, int w) {
+  KeyRange r{0, 0, qb1 + 1};
+  if (mode == kModeSA) {
+    const int ws = qb0 - w + 1 > 0 ? qb0 - w + 1 : 0;
+    r.r1_end = n_sink < ws ? n_sink : ws;
+    r.r2_beg = ws;
+  } else if (mode == kModeMiddle) {
+    r.r2_beg = n_sink;
+    r.kend = qb1 - w + 1;
+  }
+  return r;
+}
 
 // Slots of the small int32 header at the start of the workspace.
 enum Meta : int {
@@ -53,6 +84,9 @@ struct Shape {
   int64_t T;
   int32_t max_seqlen, Hq, Hkv, d, G, BMq;
   int32_t elem_bytes;
+  // work items per query tile: 1 for the routed forward (the head's own mode),
+  // 2 for the dual-mode forward (SA set and middle set of every head)
+  int32_t parts = 1;
 };
 
 Workspace plan_workspace(const Shape& s);
@@ -63,7 +97,7 @@ Workspace plan_workspace(const Shape& s);
 // unplanned (or differently planned) workspace never reads a stale list.
 inline int32_t plan_stamp(const Shape& s) {
   uint64_t h = 0x9E3779B97F4A7C15ull;
-  const int64_t v[6] = {s.B, s.T, s.Hq, s.Hkv, s.BMq, s.max_seqlen};
+  const int64_t v[7] = {s.B, s.T, s.Hq, s.Hkv, s.BMq, s.max_seqlen, s.parts};
   for (int64_t x : v) {
     h ^= static_cast<uint64_t>(x) + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
     h *= 0xBF58476D1CE4E5B9ull;
@@ -87,9 +121,27 @@ hipError_t launch_route(const void* K, bool bf16, const int32_t* cu, int32_t B, 
 hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,
                            const int32_t* cu, const Workspace& ws, char* base, hipStream_t st);
 
+// Outputs of an attention launch: items of mode FA or SA write O / lse,
+// items of the middle set O_mid / lse_mid (dual-mode forward only).
+struct AttnOut {
+  void* O;
+  float* lse;
+  void* O_mid;
+  float* lse_mid;
+};
+
 hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
-                            const void* V, const int8_t* modes, const int32_t* cu, void* O,
-                            float* lse, const Workspace& ws, char* base, hipStream_t st);
+                            const void* V, const int32_t* cu, const AttnOut& out,
+                            const Workspace& ws, char* base, hipStream_t st);
+
+// Training-forward helpers (ea_dual.hip).
+hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float tau, int64_t n,
+                               float* r_soft, int8_t* modes, hipStream_t st);
+// O_fa / lse_fa hold the middle-set partial on entry and the FA result on
+// exit; O (if not null) receives the straight-through mix selected by modes.
+hipError_t launch_dual_merge(const Shape& s, const int32_t* cu, const int8_t* modes,
+                             const void* O_sa, const float* lse_sa, void* O_fa, float* lse_fa,
+                             void* O, hipStream_t st);
 
 // Matrix-core ceiling probe (ea_probe.hip) and its FLOP count.
 hipError_t launch_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,

@@ -7,7 +7,9 @@
 // Test-time Adaptive Sparsity Ratios for Efficient Transformers").  The
 // item's cost is the number of 64-token key blocks its rows can see: all
 // causal blocks for an FA head, sink blocks plus the local window for an SA
-// head.
+// head.  The dual-mode (training) forward lists every tile twice, once over
+// its head's SA set and once over the causal blocks outside it, whose partial
+// results the merge kernel combines into the FA output (ea_dual.hip).
 //
 // Items are sorted by descending cost with a stable radix sort over the raw
 // order (KV head, sequence, query tile), so the list is longest-processing-
@@ -100,25 +102,20 @@ __device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int32_t x)
   return lo;
 }
 
-__device__ __forceinline__ int item_cost(int mode, int p0, int p1, int n_sink, int w) {
-  const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
-  if (mode == 0) return qb1 + 1;
-  const int ws = max(0, qb0 - w + 1);
-  return min(n_sink, ws) + (qb1 + 1 - ws);
-}
-
 // Sort key of a cost: 0 for the most expensive band of 2^kCostBandShift
 // blocks; max_key(nbins) for the unused slots past the item count.
 __host__ __device__ __forceinline__ uint32_t max_key(int32_t nbins) {
   return static_cast<uint32_t>(((nbins - 1) >> kCostBandShift) + 1);
 }
 
-// Raw item x (KV head major, then sequence, then query tile from the last,
-// most expensive tile down), its banded sort key and its index as the sort
-// value; the stable sort keeps this raw order inside a band.
+// Raw item x (part major, then KV head, sequence, and query tile from the
+// last, most expensive tile down), its banded sort key and its index as the
+// sort value; the stable sort keeps this raw order inside a band.  With one
+// part an item covers its head's routed mode; with two (dual-mode forward)
+// part 0 covers every head's SA set and part 1 the rest of its causal blocks.
 __global__ __launch_bounds__(256) void items_kernel(
     const int32_t* __restrict__ cu, const int8_t* __restrict__ modes, int32_t B, int32_t Hkv,
-    int32_t BMq, int32_t n_sink, const int32_t* __restrict__ meta,
+    int32_t BMq, int32_t parts, int32_t n_sink, const int32_t* __restrict__ meta,
     const int32_t* __restrict__ tile_prefix, const int32_t* __restrict__ seq_w, int32_t nbins,
     int64_t max_items, Item* __restrict__ raw, uint32_t* __restrict__ keys,
     int32_t* __restrict__ vals) {
@@ -126,23 +123,29 @@ __global__ __launch_bounds__(256) void items_kernel(
   if (x >= max_items) return;
   vals[x] = static_cast<int32_t>(x);
   const int32_t tiles = meta[kMetaTiles];
-  if (x >= static_cast<int64_t>(tiles) * Hkv) {
+  const int64_t per_part = static_cast<int64_t>(tiles) * Hkv;
+  if (x >= per_part * parts) {
     keys[x] = max_key(nbins);
     return;
   }
-  const int kvh = static_cast<int>(x / tiles);
-  const int32_t rem = static_cast<int32_t>(x - static_cast<int64_t>(kvh) * tiles);
+  const int part = static_cast<int>(x / per_part);
+  const int64_t xi = x - part * per_part;
+  const int kvh = static_cast<int>(xi / tiles);
+  const int32_t rem = static_cast<int32_t>(xi - static_cast<int64_t>(kvh) * tiles);
   const int b = find_seq(tile_prefix, B, rem);
   const int qt = (tile_prefix[b + 1] - 1) - rem;
   const int L = cu[b + 1] - cu[b];
   const int p0 = qt * BMq, p1 = min(p0 + BMq, L) - 1;
-  const int mode = modes[static_cast<int64_t>(b) * Hkv + kvh] != 0 ? 1 : 0;
-  const int cost = item_cost(mode, p0, p1, n_sink, seq_w[b]);
+  int mode;
+  if (parts == 1) mode = modes[static_cast<int64_t>(b) * Hkv + kvh] != 0 ? kModeSA : kModeFA;
+  else mode = part == 0 ? kModeSA : kModeMiddle;
+  const int cost = key_range(mode, p0 / kBlock, p1 / kBlock, n_sink, seq_w[b]).count();
   Item it;
   it.b = b;
   it.kvh = kvh;
   it.qt = qt;
   it.cost = cost;
+  it.mode = mode;
   raw[x] = it;
   keys[x] = static_cast<uint32_t>((nbins - 1 - min(cost, nbins - 1)) >> kCostBandShift);
 }
@@ -159,7 +162,7 @@ Workspace plan_workspace(const Shape& s) {
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   Workspace w{};
   w.nbins = (s.max_seqlen + kBlock - 1) / kBlock + 1;
-  w.max_items = static_cast<int64_t>(s.Hkv) * ((s.T + s.BMq - 1) / s.BMq + s.B);
+  w.max_items = static_cast<int64_t>(s.parts) * s.Hkv * ((s.T + s.BMq - 1) / s.BMq + s.B);
   size_t sort_tmp = 0;
   hipError_t e = hipcub::DeviceRadixSort::SortPairs(
       nullptr, sort_tmp, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
@@ -195,8 +198,8 @@ hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* mode
                      g.window_blocks, g.keep_fraction, plan_stamp(s), meta, tile_prefix, seq_w);
   const unsigned grid = static_cast<unsigned>((ws.max_items + 255) / 256);
   hipLaunchKernelGGL(items_kernel, dim3(grid), dim3(256), 0, st, cu, modes, s.B, s.Hkv, s.BMq,
-                     g.n_sink, meta, tile_prefix, seq_w, ws.nbins, ws.max_items, raw, keys_in,
-                     vals_in);
+                     s.parts, g.n_sink, meta, tile_prefix, seq_w, ws.nbins, ws.max_items, raw,
+                     keys_in, vals_in);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t tmp_bytes = ws.sort_tmp_bytes;

@@ -188,6 +188,58 @@ ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_
                                 float* lse, const void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* ---- Training forward ------------------------------------------------------
+ *
+ * During router training the pages feed the logits z through a Gumbel-Softmax
+ * with an annealed temperature and make hard decisions with a straight-through
+ * estimator: the forward pass uses r_hard = argmax r_soft while gradients flow
+ * through r_soft (paper body: Gumbel-Softmax and STE paragraphs of the method
+ * section; summary Sec. 2.2).  A head's output is r[0] O_FA + r[1] O_SA with
+ * r = r_hard - sg(r_soft) + r_soft, so the training forward computes every
+ * head in both modes. */
+
+/* ea_gumbel_route - r_soft and hard modes from routing logits.
+ *
+ *   logits  float32 [n, 2] device array (z of ea_route, rows (b, g) flattened)
+ *   gumbel  float32 [n, 2] standard Gumbel noise, or NULL for none
+ *   tau     temperature, finite and > 0
+ *   r_soft  out float32 [n, 2]: softmax((z + g) / tau) over the two modes, or NULL
+ *   modes   out int8 [n]: 1 (SA) iff (z1 + g1) / tau > (z0 + g0) / tau, taken in
+ *           float32 (a tie goes to FA)
+ * n >= 0.  Asynchronous on `stream`. */
+ea_status ea_gumbel_route(const float* logits, const float* gumbel, float tau, int32_t n,
+                          float* r_soft, int8_t* modes, void* stream);
+
+/* Bytes of device workspace ea_dual_prefill needs (0 if the sizes are invalid):
+ * the work list of ea_hybrid_prefill with two entries per query tile. */
+size_t ea_dual_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                      int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                      ea_dtype dtype);
+
+/* ea_dual_prefill - dual-mode attention forward: every query head in both
+ * modes in one launch, then the straight-through mix.
+ *
+ *   Q, K, V, cu_seqlens, sizes, params: as for ea_hybrid_prefill
+ *   O_fa, O_sa  out [T, Hq, head_dim] of `dtype`: each head's FA and SA output
+ *   lse_fa, lse_sa  out float32 [Hq, T]: their natural-log sums of exponentials
+ *   O       out [T, Hq, head_dim] of `dtype`, the forward value of the mix:
+ *           O_sa where modes[b, hq / (Hq / Hkv)] == 1, else O_fa; or NULL
+ *   modes   int8 [B, Hkv] hard decisions (e.g. from ea_gumbel_route); read
+ *           only when O is not NULL
+ *
+ * Every causal key block of a head is visited once: the SA set (sinks and
+ * window) gives O_SA and LSE_SA, the remaining blocks a partial that a merge
+ * pass combines with them into O_FA and LSE_FA (attention over disjoint key
+ * sets combines by their LSE weights), so the matrix work equals that of an
+ * FA-only forward.  The outputs must not alias; limits and errors are those of
+ * ea_hybrid_prefill. */
+ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                          const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                          int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                          int32_t head_dim, const ea_sparsity_params* params, void* O,
+                          void* O_fa, void* O_sa, float* lse_fa, float* lse_sa, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* ea_mfma_probe - measurement helper, not part of the attention path: the
  * practical bf16 matrix-core ceiling that the attention kernel's throughput is
  * set against beside the data-sheet peak (256 CUs x 2.4 GHz x 4096 FLOP/clk).

@@ -16,7 +16,8 @@ def test_every_header_function_is_exported():
     names = ea.header_functions()
     assert set(names) == {"ea_abi_version", "ea_last_error", "ea_route",
                           "ea_hybrid_prefill_workspace_size", "ea_hybrid_prefill",
-                          "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run", "ea_mfma_probe"}
+                          "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run", "ea_mfma_probe",
+                          "ea_gumbel_route", "ea_dual_prefill_workspace_size", "ea_dual_prefill"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -156,3 +157,54 @@ def test_mfma_probe_host_errors():
         st = L.ea_mfma_probe(c["out"], c["n"], c["iters"], 1, ctypes.byref(flops), None)
         assert st == bnd.EA_ERR_INVALID_ARG, (c, st)
         assert msg in ea.ea_last_error(), (c, ea.ea_last_error())
+
+
+def test_gumbel_route_host_errors():
+    L = ea.lib()
+    cases = [
+        ((None, None, 1.0, 4, FAKE, FAKE), "null pointer"),
+        ((FAKE, None, 1.0, 4, FAKE, None), "null pointer"),
+        ((FAKE, None, 1.0, -1, FAKE, FAKE), "n must be"),
+        ((FAKE, None, 0.0, 4, FAKE, FAKE), "tau"),
+        ((FAKE, None, -1.0, 4, FAKE, FAKE), "tau"),
+        ((FAKE, None, float("inf"), 4, FAKE, FAKE), "tau"),
+        ((FAKE, None, float("nan"), 4, FAKE, FAKE), "tau"),
+    ]
+    for args, msg in cases:
+        assert L.ea_gumbel_route(*args, None) == bnd.EA_ERR_INVALID_ARG, args
+        assert msg in ea.ea_last_error(), (args, ea.ea_last_error())
+    # n = 0: nothing to launch
+    assert L.ea_gumbel_route(FAKE, None, 1.0, 0, FAKE, FAKE, None) == 0
+
+
+def test_dual_workspace_holds_two_entries_per_tile():
+    one = ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
+    two = ea.ea_dual_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
+    items = 8 * (131072 // 64 + 1)
+    assert two - one >= items * (20 + 16) - 4096
+    assert ea.ea_dual_prefill_workspace_size(1, 1000, 1000, 30, 8, 128, 1) == 0
+
+
+def test_dual_prefill_host_errors():
+    L = ea.lib()
+    sp = bnd.SparsityParams(64, 1, 0, 0.2, 0.0)
+    A, B2, C, D2, E2, F2 = FAKE, FAKE + 256, FAKE + 512, FAKE + 768, FAKE + 1024, FAKE + 1280
+
+    def call(modes=A, O=B2, O_fa=C, O_sa=D2, lse_fa=E2, lse_sa=F2, ws_bytes=1 << 40, sp_=sp):
+        return L.ea_dual_prefill(A, A, A, 1, modes, A, 1, 1000, 1000, 8, 2, 128,
+                                 ctypes.byref(sp_), O, O_fa, O_sa, lse_fa, lse_sa, A, ws_bytes,
+                                 None)
+
+    assert call(O_sa=None) == -1 and "null pointer" in ea.ea_last_error()
+    assert call(lse_fa=None) == -1
+    assert call(O_fa=None) == -1
+    assert call(modes=None) == -1 and "modes is required" in ea.ea_last_error()
+    assert call(O_sa=C) == -1 and "alias" in ea.ea_last_error()
+    assert call(O=D2) == -1 and "alias" in ea.ea_last_error()
+    assert call(lse_sa=E2) == -1 and "alias" in ea.ea_last_error()
+    assert call(O_sa=D2 + 4) == -1 and "16-byte" in ea.ea_last_error()
+    assert call(ws_bytes=16) == -3
+    assert call(sp_=bnd.SparsityParams(32, 1, 0, 0.2, 0.0)) == -2
+    # modes may be null when the mix is not requested; zero tokens launch nothing
+    assert L.ea_dual_prefill(A, A, A, 1, None, A, 1, 0, 0, 8, 2, 128, ctypes.byref(sp), None, C,
+                             D2, E2, F2, A, 1 << 40, None) == 0
