@@ -6,6 +6,13 @@ throughput.
 """
 from .binding import (  # noqa: F401
     EAError,
+    KVCache,
+    KVCacheDesc,
+    ea_decode_step,
+    ea_decode_workspace_size,
+    ea_kvcache_bytes,
+    ea_kvcache_init,
+    ea_kvcache_prefill,
     ea_abi_version,
     ea_dual_prefill,
     ea_dual_prefill_workspace_size,

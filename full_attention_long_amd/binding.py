@@ -43,6 +43,14 @@ class SparsityParams(ctypes.Structure):
     ]
 
 
+class KVCacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("max_len", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
+        ("window_blocks", ctypes.c_int32), ("keep_fraction", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -81,6 +89,17 @@ def lib() -> ctypes.CDLL:
     L.ea_dual_prefill.restype = i32
     L.ea_dual_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                   ctypes.POINTER(SparsityParams), vp, vp, vp, vp, vp, vp, sz, vp]
+    cd = ctypes.POINTER(KVCacheDesc)
+    L.ea_kvcache_bytes.restype = sz
+    L.ea_kvcache_bytes.argtypes = [cd, vp]
+    L.ea_kvcache_init.restype = i32
+    L.ea_kvcache_init.argtypes = [cd, vp, vp, sz, vp]
+    L.ea_kvcache_prefill.restype = i32
+    L.ea_kvcache_prefill.argtypes = [cd, vp, sz, vp, vp, vp, i64, vp]
+    L.ea_decode_workspace_size.restype = sz
+    L.ea_decode_workspace_size.argtypes = [cd, i32]
+    L.ea_decode_step.restype = i32
+    L.ea_decode_step.argtypes = [cd, vp, sz, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.ea_mfma_probe.restype = i32
     L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
@@ -283,6 +302,98 @@ def ea_dual_prefill(Q, K, V, cu_seqlens, max_seqlen: int, *, modes=None, n_sink:
                                  _ptr(out_fa), _ptr(out_sa), _ptr(lse_fa), _ptr(lse_sa),
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, out_fa, out_sa, lse_fa, lse_sa
+
+
+def ea_kvcache_bytes(desc: KVCacheDesc, modes_host) -> int:
+    """Bytes of a cache for ``desc`` and the routing ``modes_host`` (a CPU int8
+    tensor [B, Hkv])."""
+    import torch
+    if modes_host.is_cuda or modes_host.dtype != torch.int8 or not modes_host.is_contiguous():
+        raise ValueError("modes_host must be a contiguous CPU int8 tensor")
+    return int(lib().ea_kvcache_bytes(ctypes.byref(desc), ctypes.c_void_p(modes_host.data_ptr())))
+
+
+def ea_kvcache_init(desc: KVCacheDesc, modes, cache, *, stream=None):
+    _dev(modes, "modes")
+    _dev(cache, "cache")
+    _check(lib().ea_kvcache_init(ctypes.byref(desc), _ptr(modes), _ptr(cache), cache.numel(),
+                                 _stream(stream)))
+    return cache
+
+
+def ea_kvcache_prefill(desc: KVCacheDesc, cache, K, V, cu_seqlens, *, stream=None):
+    for t, n in [(cache, "cache"), (K, "K"), (V, "V"), (cu_seqlens, "cu_seqlens")]:
+        _dev(t, n)
+    _check(lib().ea_kvcache_prefill(ctypes.byref(desc), _ptr(cache), cache.numel(), _ptr(K),
+                                    _ptr(V), _ptr(cu_seqlens), K.shape[0], _stream(stream)))
+    return cache
+
+
+def ea_decode_workspace_size(desc: KVCacheDesc, Hq: int) -> int:
+    return int(lib().ea_decode_workspace_size(ctypes.byref(desc), Hq))
+
+
+def ea_decode_step(desc: KVCacheDesc, cache, q, k_new, v_new, *, softmax_scale: float = 0.0,
+                   out=None, lse=None, with_lse: bool = True, workspace=None, stream=None):
+    """Append (k_new, v_new) [B, Hkv, d] at each sequence's length and attend
+    with q [B, Hq, d]; returns (O [B, Hq, d] bf16, LSE float32 [B, Hq])."""
+    import torch
+    for t, n in [(cache, "cache"), (q, "q"), (k_new, "k_new"), (v_new, "v_new")]:
+        _dev(t, n)
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, ea_decode_workspace_size(desc, Hq)), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().ea_decode_step(ctypes.byref(desc), _ptr(cache), cache.numel(), _ptr(q),
+                                _ptr(k_new), _ptr(v_new), Hq, float(softmax_scale), _ptr(out),
+                                _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+class KVCache:
+    """A mode-aware KV cache in one device buffer (bf16, blocks of 64 tokens).
+
+    FA heads keep every block; SA heads keep their sink blocks and a ring of
+    the window at ``max_len``.  ``lengths`` views the per-sequence token counts
+    kept in the buffer's header."""
+
+    def __init__(self, modes, max_len: int, head_dim: int, *, n_sink: int = 1,
+                 window_blocks: int = 0, keep_fraction: float = 0.2, stream=None):
+        import torch
+        B, Hkv = modes.shape
+        self.desc = KVCacheDesc(B, Hkv, head_dim, max_len, n_sink, window_blocks, keep_fraction)
+        m_host = modes.detach().to("cpu", torch.int8).contiguous()
+        m_dev = m_host.cuda()
+        self.nbytes = ea_kvcache_bytes(self.desc, m_host)
+        if self.nbytes == 0:
+            raise EAError(EA_ERR_INVALID_ARG, ea_last_error() or "invalid cache descriptor")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
+        ea_kvcache_init(self.desc, m_dev, self.buf, stream=stream)
+        self.workspace = None
+
+    @property
+    def lengths(self):
+        return self.buf[:4 * self.desc.B].view(torch_int32())
+
+    def prefill(self, K, V, cu_seqlens, *, stream=None):
+        return ea_kvcache_prefill(self.desc, self.buf, K, V, cu_seqlens, stream=stream)
+
+    def decode(self, q, k_new, v_new, **kw):
+        import torch
+        if self.workspace is None:
+            self.workspace = torch.empty(max(1, ea_decode_workspace_size(self.desc, q.shape[1])),
+                                         dtype=torch.uint8, device="cuda")
+        kw.setdefault("workspace", self.workspace)
+        return ea_decode_step(self.desc, self.buf, q, k_new, v_new, **kw)
+
+
+def torch_int32():
+    import torch
+    return torch.int32
 
 
 def ea_mfma_probe(out, n_workgroups: int, iters: int, *, seed: int = 1, stream=None) -> int:

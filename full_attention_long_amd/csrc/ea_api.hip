@@ -250,6 +250,155 @@ ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype 
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+ea_status check_cache_desc(const ea_kvcache_desc* c) {
+  if (!c) return fail(EA_ERR_INVALID_ARG, "null cache descriptor");
+  if (c->B < 1 || c->Hkv < 1) return fail(EA_ERR_INVALID_ARG, "B and Hkv must be >= 1");
+  if (static_cast<int64_t>(c->B) * c->Hkv > (1 << 24))
+    return fail(EA_ERR_INVALID_ARG, "B * Hkv must be <= 2^24");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->max_len < 1) return fail(EA_ERR_INVALID_ARG, "max_len must be >= 1");
+  if (c->n_sink_blocks < 0 || c->window_blocks < 0)
+    return fail(EA_ERR_INVALID_ARG, "n_sink_blocks and window_blocks must be >= 0");
+  if (c->window_blocks == 0 && !(c->keep_fraction > 0.f && c->keep_fraction <= 1.f))
+    return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1]");
+  return EA_OK;
+}
+
+ea::CacheView cache_view(const ea_kvcache_desc* d, void* cache, size_t bytes) {
+  const ea::CacheLayout l = ea::cache_layout(d->B, d->Hkv);
+  char* p = static_cast<char*>(cache);
+  ea::CacheView v{};
+  v.B = d->B;
+  v.Hkv = d->Hkv;
+  v.d = d->head_dim;
+  v.max_len = d->max_len;
+  v.n_sink = d->n_sink_blocks;
+  v.window_blocks = d->window_blocks;
+  v.keep_fraction = d->keep_fraction;
+  const size_t blk = static_cast<size_t>(2) * ea::kBlock * d->head_dim * 2;
+  v.area_blocks = bytes > l.blocks ? static_cast<int64_t>((bytes - l.blocks) / blk) : 0;
+  v.lengths = reinterpret_cast<int32_t*>(p + l.lengths);
+  v.cap = reinterpret_cast<int32_t*>(p + l.cap);
+  v.ring = reinterpret_cast<int32_t*>(p + l.ring);
+  v.base = reinterpret_cast<int64_t*>(p + l.base);
+  v.mode = reinterpret_cast<int8_t*>(p + l.mode);
+  v.valid = reinterpret_cast<int32_t*>(p + l.valid);
+  v.K = reinterpret_cast<uint16_t*>(p + l.blocks);
+  v.V = v.K + static_cast<size_t>(ea::kBlock) * d->head_dim;
+  return v;
+}
+
+ea_status check_cache_buffer(const ea_kvcache_desc* d, const void* cache, size_t bytes) {
+  if (!cache) return fail(EA_ERR_INVALID_ARG, "null cache");
+  if ((reinterpret_cast<uintptr_t>(cache) & 255u) != 0)
+    return fail(EA_ERR_INVALID_ARG, "cache must be 256-byte aligned");
+  if (bytes < ea::cache_layout(d->B, d->Hkv).blocks)
+    return fail(EA_ERR_WORKSPACE, "cache of %zu bytes is smaller than its header", bytes);
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ea_kvcache_bytes(const ea_kvcache_desc* desc, const int8_t* modes_host) {
+  if (check_cache_desc(desc) != EA_OK || !modes_host) return 0;
+  g_err.clear();
+  int64_t blocks = 0;
+  const int64_t ns = static_cast<int64_t>(desc->B) * desc->Hkv;
+  for (int64_t s = 0; s < ns; ++s)
+    blocks += ea::cache_slot_blocks(modes_host[s], desc->max_len, desc->n_sink_blocks,
+                                    desc->window_blocks, desc->keep_fraction);
+  return ea::cache_layout(desc->B, desc->Hkv).blocks +
+         static_cast<size_t>(blocks) * 2 * ea::kBlock * desc->head_dim * 2;
+}
+
+ea_status ea_kvcache_init(const ea_kvcache_desc* desc, const int8_t* modes, void* cache,
+                          size_t bytes, void* stream) {
+  ea_status st = check_cache_desc(desc);
+  if (st != EA_OK) return st;
+  if (!modes) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if ((st = check_cache_buffer(desc, cache, bytes)) != EA_OK) return st;
+  hipError_t e = ea::launch_cache_init(cache_view(desc, cache, bytes), modes,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "cache init launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ea_status ea_kvcache_prefill(const ea_kvcache_desc* desc, void* cache, size_t bytes,
+                             const void* K, const void* V, const int32_t* cu_seqlens,
+                             int64_t total_tokens, void* stream) {
+  ea_status st = check_cache_desc(desc);
+  if (st != EA_OK) return st;
+  if ((st = check_cache_buffer(desc, cache, bytes)) != EA_OK) return st;
+  if (!K || !V || !cu_seqlens) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(K) || !aligned16(V)) return fail(EA_ERR_INVALID_ARG, "K and V must be 16-byte aligned");
+  if (total_tokens < 0 || total_tokens >= (int64_t(1) << 31))
+    return fail(EA_ERR_INVALID_ARG, "total_tokens must be in [0, 2^31)");
+  hipError_t e = ea::launch_cache_fill(cache_view(desc, cache, bytes), cu_seqlens, total_tokens,
+                                       K, V, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "cache fill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static int32_t decode_chunks(const ea_kvcache_desc* d) {
+  const int32_t NB = (d->max_len + ea::kBlock - 1) / ea::kBlock;
+  return (NB + ea::kDecodeChunkBlocks - 1) / ea::kDecodeChunkBlocks;
+}
+
+size_t ea_decode_workspace_size(const ea_kvcache_desc* desc, int32_t Hq) {
+  if (check_cache_desc(desc) != EA_OK || Hq < 1) return 0;
+  g_err.clear();
+  const size_t rows = static_cast<size_t>(desc->B) * Hq * decode_chunks(desc);
+  return ((rows * desc->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)) +
+         rows * sizeof(float);
+}
+
+ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes, const void* q,
+                         const void* k_new, const void* v_new, int32_t Hq, float softmax_scale,
+                         void* O, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  ea_status st = check_cache_desc(desc);
+  if (st != EA_OK) return st;
+  if ((st = check_cache_buffer(desc, cache, bytes)) != EA_OK) return st;
+  if (!q || !k_new || !v_new || !O) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(O))
+    return fail(EA_ERR_INVALID_ARG, "q, k_new, v_new and O must be 16-byte aligned");
+  if (Hq < 1 || Hq % desc->Hkv != 0)
+    return fail(EA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, desc->Hkv);
+  if (Hq / desc->Hkv > 16) return fail(EA_ERR_UNSUPPORTED, "Hq / Hkv must be <= 16 for decode");
+  if (!(softmax_scale >= 0.f) || isinf(softmax_scale))
+    return fail(EA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  const size_t need = ea_decode_workspace_size(desc, Hq);
+  if (!workspace || workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  ea::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.O = static_cast<uint16_t*>(O);
+  a.lse = lse;
+  a.Hq = Hq;
+  a.G = Hq / desc->Hkv;
+  a.n_chunks = decode_chunks(desc);
+  a.chunk_blocks = ea::kDecodeChunkBlocks;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(desc->head_dim));
+  const size_t rows = static_cast<size_t>(desc->B) * Hq * a.n_chunks;
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        ((rows * desc->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)));
+  hipError_t e = ea::launch_decode(cache_view(desc, cache, bytes), a, k_new, v_new,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ea_status ea_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,
                         int64_t* flops, void* stream) {
   if (!out) return fail(EA_ERR_INVALID_ARG, "null pointer argument");

@@ -134,6 +134,51 @@ hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, co
                             const void* V, const int32_t* cu, const AttnOut& out,
                             const Workspace& ws, char* base, hipStream_t st);
 
+// Mode-aware KV cache (ea_decode.hip): the device view of a cache buffer.
+struct CacheView {
+  int32_t B, Hkv, d, max_len, n_sink, window_blocks;
+  float keep_fraction;
+  int64_t area_blocks;   // 64-token blocks the caller's buffer has room for
+  int32_t* lengths;      // [B] tokens held per sequence
+  int32_t* cap;          // [B * Hkv] slot capacity in blocks
+  int32_t* ring;         // [B * Hkv] ring size in blocks past the sinks, 0 = no ring
+  int64_t* base;         // [B * Hkv] first block of the slot
+  int8_t* mode;          // [B * Hkv] 0 = FA, 1 = SA
+  int32_t* valid;        // [1] 1 once the slot table fits the buffer
+  uint16_t* K;           // block pb: K rows at K + pb * 2 * 64 * d, V rows 64 * d later
+  uint16_t* V;           // = K + 64 * d
+};
+
+// Byte layout of a cache buffer: the header (a function of B and Hkv) and the
+// blocks after it, each 64 K rows then 64 V rows of d bf16 values.
+struct CacheLayout {
+  size_t lengths, cap, ring, base, mode, valid, blocks;
+};
+CacheLayout cache_layout(int32_t B, int32_t Hkv);
+// Slot capacity in blocks for a KV head of the given mode.
+int32_t cache_slot_blocks(int mode, int32_t max_len, int32_t n_sink, int32_t window_blocks,
+                          float keep_fraction);
+
+// Arguments of one decode step (one query token per sequence).
+struct DecodeArgs {
+  const uint16_t* q;   // [B, Hq, d] bf16
+  uint16_t* O;         // [B, Hq, d] bf16
+  float* lse;          // [B, Hq] or null
+  float* o_part;       // [B, Hq, n_chunks, d] chunk partials (workspace)
+  float* lse_part;     // [B, Hq, n_chunks]
+  int32_t Hq, G, n_chunks, chunk_blocks;
+  float scale;
+};
+
+// Key blocks per decode chunk (one workgroup of the split over the cache).
+constexpr int kDecodeChunkBlocks = 16;
+
+hipError_t launch_cache_init(const CacheView& c, const int8_t* modes, hipStream_t st);
+hipError_t launch_cache_fill(const CacheView& c, const int32_t* cu, int64_t T, const void* K,
+                             const void* V, hipStream_t st);
+hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, const void* k_new,
+                         const void* v_new, hipStream_t st);
+
 // Training-forward helpers (ea_dual.hip).
 hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float tau, int64_t n,
                                float* r_soft, int8_t* modes, hipStream_t st);

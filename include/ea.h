@@ -240,6 +240,67 @@ ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype 
                           void* O_fa, void* O_sa, float* lse_fa, float* lse_sa, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ---- Decode with a mode-aware KV cache -------------------------------------
+ *
+ * One new token per sequence attends to its cached keys with the prefill's
+ * visibility rule for a query at the last position of a sequence one token
+ * longer (paper body: FA and SA equations, hybrid-head output equation).  An
+ * FA head's cache slot holds every block; an SA head's holds its sink blocks
+ * and a ring of R blocks, R = the window at max_len (the window never moves
+ * back, so a block that leaves it is never needed again): at keep_fraction
+ * 0.2 an SA slot is about a fifth of an FA slot.  Blocks are 64 tokens; the
+ * cache is bfloat16; one sequence's slots follow its routing modes, fixed
+ * when the cache is initialised. */
+typedef struct {
+  int32_t B;              /* sequences */
+  int32_t Hkv;            /* KV heads */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t max_len;        /* tokens a sequence may reach, >= 1 */
+  int32_t n_sink_blocks;  /* as in ea_sparsity_params */
+  int32_t window_blocks;  /* > 0: fixed window; 0: from keep_fraction per length */
+  float keep_fraction;    /* in (0, 1], read when window_blocks == 0 */
+} ea_kvcache_desc;
+
+/* Bytes of a cache for `desc` with the routing `modes_host` (int8 [B, Hkv] in
+ * HOST memory, 0 = FA, 1 = SA); 0 if desc is invalid. */
+size_t ea_kvcache_bytes(const ea_kvcache_desc* desc, const int8_t* modes_host);
+
+/* ea_kvcache_init - lay out an empty cache in `cache` (device buffer of
+ * `bytes`, 256-byte aligned) for the routing `modes` (int8 [B, Hkv] DEVICE
+ * memory, the same values ea_kvcache_bytes was given): slot table, zeroed
+ * blocks, lengths 0.  A buffer smaller than the layout needs leaves the cache
+ * marked unusable (later calls then write nothing and decode outputs zeros). */
+ea_status ea_kvcache_init(const ea_kvcache_desc* desc, const int8_t* modes, void* cache,
+                          size_t bytes, void* stream);
+
+/* ea_kvcache_prefill - store a packed prompt batch (K, V [T, Hkv, head_dim]
+ * bf16, cu_seqlens int32 [B + 1], T = total_tokens) into the cache: every row
+ * an FA head or a later SA query can see; lengths[b] = L_b.  L_b <= max_len
+ * is a precondition (a longer sequence's slots are left untouched). */
+ea_status ea_kvcache_prefill(const ea_kvcache_desc* desc, void* cache, size_t bytes,
+                             const void* K, const void* V, const int32_t* cu_seqlens,
+                             int64_t total_tokens, void* stream);
+
+/* Bytes of device workspace ea_decode_step needs (chunk partials of the split
+ * over the cache); 0 if the sizes are invalid. */
+size_t ea_decode_workspace_size(const ea_kvcache_desc* desc, int32_t Hq);
+
+/* ea_decode_step - append one token per sequence and attend with it.
+ *
+ *   q             [B, Hq, head_dim] bf16: the new token's queries
+ *   k_new, v_new  [B, Hkv, head_dim] bf16: its keys and values, stored at
+ *                 position lengths[b] before the attention
+ *   softmax_scale > 0, or 0 for 1/sqrt(head_dim)
+ *   O             out [B, Hq, head_dim] bf16
+ *   lse           out float32 [B, Hq] natural-log sums of exponentials, or NULL
+ * Then lengths[b] += 1.  Hq must be a multiple of Hkv with Hq / Hkv <= 16;
+ * lengths[b] < max_len is a precondition (a full sequence gets O = 0 and
+ * keeps its length). */
+ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes, const void* q,
+                         const void* k_new, const void* v_new, int32_t Hq, float softmax_scale,
+                         void* O, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* ea_mfma_probe - measurement helper, not part of the attention path: the
  * practical bf16 matrix-core ceiling that the attention kernel's throughput is
  * set against beside the data-sheet peak (256 CUs x 2.4 GHz x 4096 FLOP/clk).

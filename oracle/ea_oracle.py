@@ -16,6 +16,8 @@ What is computed, and where the pages define it:
 * Hard routing r_hard = argmax over the two columns, 0 = FA, 1 = SA (router
   paragraph on Fig. 3(b) and the Gumbel-Softmax paragraph: inference uses
   hard decisions).
+* Decode: the newest token of each sequence attends to its history with the
+  same visibility as the last row of the prefill of that longer sequence.
 * Training-time routing: r_soft = Gumbel-Softmax of z (softmax over the two
   modes of (z + g) / tau, g standard Gumbel noise, tau the annealed
   temperature), r_hard = argmax of r_soft, and the straight-through estimator
@@ -255,6 +257,39 @@ def attention_weights(Q, K, modes, L, hq, *, G, block=64, n_sink=1, window_block
     _, _, P = _attend(Q[:L, hq], np.arange(L), K[:L, g], Vdummy, int(modes[0, g]), ns, w, block,
                       _scale(d, softmax_scale), return_weights=True)
     return P
+
+
+# ----------------------------------------------------------------------------
+# Decode: one new token per sequence
+# ----------------------------------------------------------------------------
+
+
+def decode_attention(q_new, K_hist, V_hist, modes, *, block=64, n_sink=1, window_blocks=0,
+                     keep_fraction=0.2, softmax_scale=0.0):
+    """Attention of each sequence's newest token over its whole history.
+
+    q_new [B, Hq, d]; K_hist[b], V_hist[b] [L_b + 1, Hkv, d] hold the keys and
+    values of positions 0..L_b, the last row being the new token's.  The query
+    at position L_b sees keys as the last row of a sequence of length L_b + 1
+    in the prefill (FA and SA equations; the SA window is that of length
+    L_b + 1).  Returns (O float64 [B, Hq, d], LSE float64 [B, Hq])."""
+    B, Hq, d = q_new.shape
+    Hkv = K_hist[0].shape[1]
+    G = Hq // Hkv
+    scale = _scale(d, softmax_scale)
+    O = np.zeros((B, Hq, d), dtype=np.float64)
+    LSE = np.zeros((B, Hq), dtype=np.float64)
+    for b in range(B):
+        n = K_hist[b].shape[0]
+        ns, w = sa_geometry(n, block, n_sink, window_blocks, keep_fraction)
+        pos = np.array([n - 1])
+        for hq in range(Hq):
+            g = hq // G
+            o, lse = _attend(q_new[b, hq][None], pos, K_hist[b][:, g], V_hist[b][:, g],
+                             int(modes[b, g]), ns, w, block, scale)
+            O[b, hq] = o[0]
+            LSE[b, hq] = lse[0]
+    return O, LSE
 
 
 # ----------------------------------------------------------------------------

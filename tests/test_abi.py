@@ -17,7 +17,9 @@ def test_every_header_function_is_exported():
     assert set(names) == {"ea_abi_version", "ea_last_error", "ea_route",
                           "ea_hybrid_prefill_workspace_size", "ea_hybrid_prefill",
                           "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run", "ea_mfma_probe",
-                          "ea_gumbel_route", "ea_dual_prefill_workspace_size", "ea_dual_prefill"}
+                          "ea_gumbel_route", "ea_dual_prefill_workspace_size", "ea_dual_prefill",
+                          "ea_kvcache_bytes", "ea_kvcache_init", "ea_kvcache_prefill",
+                          "ea_decode_workspace_size", "ea_decode_step"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -208,3 +210,60 @@ def test_dual_prefill_host_errors():
     # modes may be null when the mix is not requested; zero tokens launch nothing
     assert L.ea_dual_prefill(A, A, A, 1, None, A, 1, 0, 0, 8, 2, 128, ctypes.byref(sp), None, C,
                              D2, E2, F2, A, 1 << 40, None) == 0
+
+
+def _desc(**kw):
+    d = dict(B=1, Hkv=2, head_dim=128, max_len=131072, n_sink_blocks=1, window_blocks=0,
+             keep_fraction=0.2)
+    d.update(kw)
+    return bnd.KVCacheDesc(*[d[k] for k in ["B", "Hkv", "head_dim", "max_len", "n_sink_blocks",
+                                            "window_blocks", "keep_fraction"]])
+
+
+def test_kvcache_bytes_mode_aware():
+    import torch
+    blk = 2 * 64 * 128 * 2                      # K and V rows of one 64-token block
+    fa_fa = ea.ea_kvcache_bytes(_desc(), torch.zeros((1, 2), dtype=torch.int8))
+    fa_sa = ea.ea_kvcache_bytes(_desc(), torch.tensor([[0, 1]], dtype=torch.int8))
+    # FA slot: all 2048 blocks; SA slot: 1 sink + w(2048) = 409 window blocks
+    assert fa_fa - fa_sa == (2048 - 410) * blk
+    header = fa_fa - 2 * 2048 * blk
+    assert 0 < header <= 4096
+    # a window that covers the sequence keeps every block
+    small = _desc(max_len=640, window_blocks=20)
+    assert ea.ea_kvcache_bytes(small, torch.tensor([[1, 1]], dtype=torch.int8)) == \
+        ea.ea_kvcache_bytes(small, torch.zeros((1, 2), dtype=torch.int8))
+    # a fixed window: sinks + window
+    fixed = _desc(max_len=64 * 100, window_blocks=7, n_sink_blocks=2)
+    assert ea.ea_kvcache_bytes(fixed, torch.zeros((1, 2), dtype=torch.int8)) - \
+        ea.ea_kvcache_bytes(fixed, torch.tensor([[0, 1]], dtype=torch.int8)) == (100 - 9) * blk
+    # invalid descriptors -> 0
+    z = torch.zeros((1, 2), dtype=torch.int8)
+    for bad in (dict(head_dim=96), dict(keep_fraction=0.0), dict(max_len=0), dict(B=0),
+                dict(n_sink_blocks=-1)):
+        assert ea.ea_kvcache_bytes(_desc(**bad), z) == 0, bad
+
+
+def test_kvcache_and_decode_host_errors():
+    L = ea.lib()
+    d = _desc()
+    ws = ea.ea_decode_workspace_size(d, 8)
+    assert ws >= 1 * 8 * 128 * 128 * 4          # chunk partials: B x Hq x chunks x d floats
+    A = FAKE
+    assert L.ea_kvcache_init(ctypes.byref(d), None, A, 1 << 30, None) == -1
+    assert L.ea_kvcache_init(ctypes.byref(d), A, A + 16, 1 << 30, None) == -1
+    assert "256-byte" in ea.ea_last_error()
+    assert L.ea_kvcache_init(ctypes.byref(d), A, A, 16, None) == -3
+    assert L.ea_kvcache_prefill(ctypes.byref(d), A, 1 << 30, None, A, A, 10, None) == -1
+
+    def step(Hq=8, scale=0.0, ws_bytes=ws, q=A, d_=d):
+        return L.ea_decode_step(ctypes.byref(d_), A, 1 << 30, q, A, A, Hq, scale, A, None, A,
+                                ws_bytes, None)
+
+    assert step(q=None) == -1
+    assert step(Hq=7) == -1 and "multiple" in ea.ea_last_error()
+    assert step(Hq=2 * 17) == -2 and "16" in ea.ea_last_error()
+    assert step(scale=-1.0) == -1
+    assert step(ws_bytes=16) == -3
+    assert step(q=A + 8) == -1 and "16-byte" in ea.ea_last_error()
+    assert step(d_=_desc(head_dim=80)) == -2

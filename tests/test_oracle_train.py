@@ -143,3 +143,39 @@ def test_dual_rows_api_equals_full():
         np.testing.assert_allclose(rows[k], full[k][toks][:, heads], rtol=0, atol=1e-14)
     for k in range(3, 5):
         np.testing.assert_allclose(rows[k], full[k][heads][:, toks].T, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Decode
+# ----------------------------------------------------------------------------
+
+def test_decode_is_the_last_prefill_row():
+    # decoding token L of a sequence equals row L of the prefill of length L + 1
+    lengths = [1, 64, 65, 200, 777]
+    Hq, Hkv, d = 4, 2, 16
+    q_new = _rand(50, len(lengths), Hq, d)
+    Kh = [_rand(60 + i, L + 1, Hkv, d) for i, L in enumerate(lengths)]
+    Vh = [_rand(80 + i, L + 1, Hkv, d) for i, L in enumerate(lengths)]
+    modes = np.array([[0, 1], [1, 0], [1, 1], [0, 1], [1, 0]], np.int8)
+    for geom in (dict(n_sink=1, keep_fraction=0.2), dict(n_sink=2, window_blocks=3),
+                 dict(n_sink=0, window_blocks=1)):
+        O, LSE = orc.decode_attention(q_new, Kh, Vh, modes, **geom)
+        for b, L in enumerate(lengths):
+            Q = np.zeros((L + 1, Hq, d))
+            Q[L] = q_new[b]
+            full, full_lse = orc.hybrid_attention(Q, Kh[b], Vh[b], modes[b:b + 1],
+                                                  np.array([0, L + 1]), **geom)
+            np.testing.assert_allclose(O[b], full[L], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(LSE[b], full_lse[:, L], rtol=0, atol=1e-13)
+
+
+def test_decode_fa_is_sdpa_over_the_history():
+    L, Hq, Hkv, d = 300, 8, 2, 16
+    q_new = _rand(90, 1, Hq, d)
+    Kh, Vh = [_rand(91, L + 1, Hkv, d)], [_rand(92, L + 1, Hkv, d)]
+    O, _ = orc.decode_attention(q_new, Kh, Vh, np.zeros((1, Hkv), np.int8))
+    q = torch.from_numpy(q_new[0])[:, None]                        # [Hq, 1, d]
+    k = torch.from_numpy(Kh[0]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    v = torch.from_numpy(Vh[0]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[:, 0]
+    np.testing.assert_allclose(O[0], ref.numpy(), rtol=0, atol=1e-12)
