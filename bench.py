@@ -312,6 +312,102 @@ def bench_dual(args):
     print(json.dumps(out), flush=True)
 
 
+def decode_bytes(lengths, modes, Hq, Hkv, d, n_sink, keep_fraction, window_blocks=0):
+    """Algorithmic HBM bytes of one decode step: the K and V rows every query
+    must read (FA: all of the sequence; SA: sink blocks and the window, as for
+    the last row of the prefill of the longer sequence), the new K/V rows
+    written, q read, O written (bf16) and the LSE (fp32)."""
+    from full_attention_long_amd import metrics
+    total = 0
+    for b, L in enumerate(lengths):
+        n = int(L) + 1                      # history including the new token
+        N = -(-n // 64)
+        w = window_blocks or metrics.window_blocks(n, n_sink, keep_fraction)
+        qb = (n - 1) // 64
+        for g in range(Hkv):
+            if modes[b, g] == 0:
+                keys = n
+            else:
+                ws = max(0, qb - w + 1)
+                sinks = min(n_sink, ws) * 64
+                keys = sinks + (n - ws * 64)
+            total += keys * d * 2 * 2
+        del N
+    B = len(lengths)
+    total += B * Hkv * d * 2 * 2             # new K/V rows
+    total += B * Hq * d * 2 * 2 + B * Hq * 4  # q in, O out, LSE
+    return total
+
+
+def bench_decode(args):
+    """Decode steps over a mode-aware KV cache holding a long prompt: one
+    token per sequence per step (append + split attention + combine); prints
+    one JSON line of its own with the HBM roofline of the step."""
+    import torch
+
+    import full_attention_long_amd as ea
+    from workloads import gen
+    from workloads.configs import WORKLOADS
+    lines = []
+    for name in args.runs.split(","):
+        c = gen.build_case(WORKLOADS[name])
+        modes = c.target_modes
+        lengths = [int(x) for x in c.lengths]
+        max_len = max(lengths) + args.steps + args.warmup + 64
+        cache = ea.KVCache(torch.from_numpy(modes), max_len, c.d, n_sink=c.n_sink,
+                           keep_fraction=c.keep_fraction)
+        fa_bytes = ea.ea_kvcache_bytes(cache.desc, torch.zeros_like(torch.from_numpy(modes)))
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+        cache.prefill(bf(c.k), bf(c.v), torch.from_numpy(c.cu_seqlens.astype(np.int32)).cuda())
+        B, Hq, Hkv, d = c.B, c.Hq, c.Hkv, c.d
+        g = torch.Generator(device="cuda").manual_seed(1)
+        q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+        kn = torch.randn((B, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        vn = torch.randn((B, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        O = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        for _ in range(args.warmup):
+            cache.decode(q, kn, vn, out=O, lse=lse)
+        torch.cuda.synchronize()
+        start_len = cache.lengths.cpu().numpy().copy()
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        evs = [(E(), E()) for _ in range(args.steps)]
+        for s in range(args.steps):
+            evs[s][0].record()
+            cache.decode(q, kn, vn, out=O, lse=lse)
+            evs[s][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        nbytes = np.mean([decode_bytes(start_len + s, modes, Hq, Hkv, d, c.n_sink,
+                                       c.keep_fraction) for s in range(args.steps)])
+        med = float(np.median(ms))
+        gbps = nbytes / (med * 1e-3) / 1e9
+        log(f"decode {name}: {med * 1e3:.1f} us per step, {nbytes / 1e6:.1f} MB -> {gbps:.0f} GB/s; "
+            f"cache {cache.nbytes / 2**20:.0f} MiB vs {fa_bytes / 2**20:.0f} MiB all-FA")
+        lines.append({"workload": name, "B": B, "context": max(lengths), "Hq": Hq, "Hkv": Hkv,
+                      "d": d, "sa_kv_heads": int(modes.sum()), "step_us_median": round(med * 1e3, 2),
+                      "bytes_per_step": int(nbytes), "gbps": round(gbps, 1),
+                      "cache_bytes": int(cache.nbytes), "cache_bytes_all_fa": int(fa_bytes)})
+        del cache
+        torch.cuda.empty_cache()
+    tot_bytes = sum(r["bytes_per_step"] for r in lines)
+    tot_us = sum(r["step_us_median"] for r in lines)
+    gbps = tot_bytes / (tot_us * 1e-6) / 1e9
+    peak = 8000.0
+    out = {
+        "metric": "decode step HBM throughput over the mode-aware KV cache (GB/s)",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(tot_us / len(lines) / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "+".join(r["workload"] for r in lines) + ":decode", "runs": lines},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(gbps / peak, 4), "traffic": None,
+                     "kernel": "ea_decode_step (append + decode_attn_kernel + combine)"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calibrate(mib):
     """One elementwise kernel of known traffic (reads and writes mib MiB), so
     that profiler byte counters can be scaled to bytes."""
@@ -374,6 +470,10 @@ def main():
                     help="measure the dual-mode (training) forward of the first --runs workload "
                          "instead (default qwen4b_s128k_sa6)")
     ap.add_argument("--tau", type=float, default=1.0, help="Gumbel-Softmax temperature (--dual)")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure decode steps over a mode-aware KV cache holding each --runs "
+                         "workload as the prompt instead (default qwen4b_s128k_sa2,sa6 and "
+                         "varlen8)")
     ap.add_argument("--calibrate-mib", type=int, default=0,
                     help="first run one elementwise kernel that reads and writes this many MiB "
                          "(for scaling profiler byte counters)")
@@ -397,6 +497,11 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_mib:
         calibrate(args.calibrate_mib)
+    if args.decode:
+        if args.runs == ",".join(DEFAULT_RUNS):
+            args.runs = "qwen4b_s128k_sa2,qwen4b_s128k_sa6,varlen8"
+        bench_decode(args)
+        return
     if args.dual:
         if args.runs == ",".join(DEFAULT_RUNS):
             args.runs = "qwen4b_s128k_sa6"

@@ -262,6 +262,8 @@ ea_status check_cache_desc(const ea_kvcache_desc* c) {
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
   if (c->max_len < 1) return fail(EA_ERR_INVALID_ARG, "max_len must be >= 1");
+  if (c->max_len > 2048 * ea::kDecodeChunkBlocks * ea::kBlock)
+    return fail(EA_ERR_UNSUPPORTED, "max_len must be <= %d", 2048 * ea::kDecodeChunkBlocks * ea::kBlock);
   if (c->n_sink_blocks < 0 || c->window_blocks < 0)
     return fail(EA_ERR_INVALID_ARG, "n_sink_blocks and window_blocks must be >= 0");
   if (c->window_blocks == 0 && !(c->keep_fraction > 0.f && c->keep_fraction <= 1.f))

@@ -319,29 +319,59 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attn_kernel(CacheView c
   }
 }
 
-// Final O and LSE of one (sequence, query head) from its chunks' partials;
-// the (b, 0) workgroup then advances lengths[b] past the new token.
+// Final O and LSE of one (sequence, query head) from its chunks' partials,
+// one workgroup per 32 of the D dims: the chunk LSEs are reduced to their max
+// and weights by the whole workgroup, then each of its 8 thread groups sums
+// every 8th chunk for the 32 dims and the groups' sums are added.  The
+// (b, 0, 0) workgroup then advances lengths[b] past the new token.
+constexpr int kCombineDims = 32;
+constexpr int kCombineGroups = 256 / kCombineDims;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(CacheView c, DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(CacheView c, DecodeArgs a) {
+  constexpr int kMaxChunks = 2048;
+  __shared__ float wgt[kMaxChunks];
+  __shared__ float red[8];
+  __shared__ float acc_s[kCombineGroups][kCombineDims];
+  const int hq = blockIdx.x, b = blockIdx.y, slice = blockIdx.z, tid = threadIdx.x;
   const int64_t p0 = (static_cast<int64_t>(b) * a.Hq + hq) * a.n_chunks;
-  float M = -INFINITY;
-  for (int k = 0; k < a.n_chunks; ++k) M = fmaxf(M, a.lse_part[p0 + k]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int k = 0; k < a.n_chunks; ++k) {
-      const float lk = a.lse_part[p0 + k];
-      if (lk == -INFINITY) continue;
-      const float e = expf(lk - M);
-      L += e;
-      acc += e * a.o_part[(p0 + k) * D + dim];
-    }
-  }
-  const int64_t orow = (static_cast<int64_t>(b) * a.Hq + hq) * D;
-  a.O[orow + dim] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(L > 0.f ? acc / L : 0.f));
-  if (dim == 0 && a.lse) a.lse[static_cast<int64_t>(b) * a.Hq + hq] = L > 0.f ? M + logf(L) : -INFINITY;
+  const int nc = a.n_chunks;  // <= kMaxChunks, checked on the host
+  float mx = -INFINITY;
+  for (int k = tid; k < nc; k += 256) mx = fmaxf(mx, a.lse_part[p0 + k]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (tid % 64 == 0) red[tid / 64] = mx;
   __syncthreads();
-  if (hq == 0 && dim == 0 && c.valid[0] && c.lengths[b] < c.max_len) c.lengths[b] += 1;
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float ls = 0.f;
+  for (int k = tid; k < nc; k += 256) {
+    const float lk = a.lse_part[p0 + k];
+    const float e = (M == -INFINITY || lk == -INFINITY) ? 0.f : expf(lk - M);
+    wgt[k] = e;
+    ls += e;
+  }
+  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off, 64);
+  if (tid % 64 == 0) red[4 + tid / 64] = ls;
+  __syncthreads();
+  const float L = red[4] + red[5] + red[6] + red[7];
+  const int dl = tid % kCombineDims, grp = tid / kCombineDims;
+  const int dim = slice * kCombineDims + dl;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int k = grp; k < nc; k += kCombineGroups) {
+    const float e = wgt[k];
+    if (e != 0.f) acc += e * a.o_part[(p0 + k) * D + dim];
+  }
+  acc_s[grp][dl] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < kCombineGroups; ++g) o += acc_s[g][dl];
+    const int64_t orow = (static_cast<int64_t>(b) * a.Hq + hq) * D;
+    a.O[orow + dim] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(L > 0.f ? o / L : 0.f));
+    if (dim == 0 && a.lse) a.lse[static_cast<int64_t>(b) * a.Hq + hq] = L > 0.f ? M + logf(L) : -INFINITY;
+    if (hq == 0 && dim == 0 && c.valid[0] && c.lengths[b] < c.max_len) c.lengths[b] += 1;
+  }
 }
 
 }  // namespace
@@ -397,10 +427,12 @@ hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, const void* k_
                   static_cast<unsigned>(c.B));
   if (c.d == 128) {
     hipLaunchKernelGGL((decode_attn_kernel<128>), grid, dim3(kDecodeThreads), 0, st, c, a);
-    hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(a.Hq, c.B), dim3(128), 0, st, c, a);
+    hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(a.Hq, c.B, 128 / kCombineDims), dim3(256),
+                       0, st, c, a);
   } else {
     hipLaunchKernelGGL((decode_attn_kernel<64>), grid, dim3(kDecodeThreads), 0, st, c, a);
-    hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(a.Hq, c.B), dim3(64), 0, st, c, a);
+    hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(a.Hq, c.B, 64 / kCombineDims), dim3(256),
+                       0, st, c, a);
   }
   return hipGetLastError();
 }

@@ -255,7 +255,7 @@ typedef struct {
   int32_t B;              /* sequences */
   int32_t Hkv;            /* KV heads */
   int32_t head_dim;       /* 64 or 128 */
-  int32_t max_len;        /* tokens a sequence may reach, >= 1 */
+  int32_t max_len;        /* tokens a sequence may reach, 1 .. 2^21 */
   int32_t n_sink_blocks;  /* as in ea_sparsity_params */
   int32_t window_blocks;  /* > 0: fixed window; 0: from keep_fraction per length */
   float keep_fraction;    /* in (0, 1], read when window_blocks == 0 */

@@ -240,7 +240,7 @@ def test_kvcache_bytes_mode_aware():
     # invalid descriptors -> 0
     z = torch.zeros((1, 2), dtype=torch.int8)
     for bad in (dict(head_dim=96), dict(keep_fraction=0.0), dict(max_len=0), dict(B=0),
-                dict(n_sink_blocks=-1)):
+                dict(n_sink_blocks=-1), dict(max_len=2**21 + 1)):
         assert ea.ea_kvcache_bytes(_desc(**bad), z) == 0, bad
 
 
