@@ -42,10 +42,12 @@ if ROOT not in sys.path:
 
 METRIC = "hybrid prefill effective TFLOP/s + ms/layer at 128K; % bf16 MFMA roofline"
 DEFAULT_RUNS = ["qwen4b_s128k_sa2", "qwen4b_s128k_sa6"]
-# The sources that decide the attention kernel's memory traffic: the kernel and
-# the work-list order that places its workgroups on the XCDs.
+# The sources that decide the attention kernel's memory traffic: the kernel,
+# the work-list order that places its workgroups on the XCDs, and the tiling
+# constants of the shared header.
 ATTN_SRCS = [os.path.join(ROOT, "full_attention_long_amd", "csrc", f)
-             for f in ("ea_attention.hip", "ea_worklist.hip", "ea_internal.h")]
+             for f in ("ea_attention.hip", "ea_worklist.hip")]
+ATTN_HEADER = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_internal.h")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attention_traffic.json")
 ATTN_KERNEL = "attention_kernel"
 CALIB_KERNEL = "bitwise_not"
@@ -91,6 +93,9 @@ def kernel_source_hash() -> str:
     for path in ATTN_SRCS:
         with open(path, "rb") as f:
             h.update(f.read())
+    with open(ATTN_HEADER) as f:
+        consts = [ln.strip() for ln in f if ln.strip().startswith("constexpr int k")]
+    h.update("\n".join(consts).encode())
     return h.hexdigest()[:16]
 
 
