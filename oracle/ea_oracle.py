@@ -16,6 +16,8 @@ What is computed, and where the pages define it:
 * Hard routing r_hard = argmax over the two columns, 0 = FA, 1 = SA (router
   paragraph on Fig. 3(b) and the Gumbel-Softmax paragraph: inference uses
   hard decisions).
+* Backward: gradients of the layer output with respect to Q, K and V, every
+  head in its routed mode (the chain rule through the FA / SA equations).
 * Decode: the newest token of each sequence attends to its history with the
   same visibility as the last row of the prefill of that longer sequence.
 * Training-time routing: r_soft = Gumbel-Softmax of z (softmax over the two
@@ -257,6 +259,55 @@ def attention_weights(Q, K, modes, L, hq, *, G, block=64, n_sink=1, window_block
     _, _, P = _attend(Q[:L, hq], np.arange(L), K[:L, g], Vdummy, int(modes[0, g]), ns, w, block,
                       _scale(d, softmax_scale), return_weights=True)
     return P
+
+
+# ----------------------------------------------------------------------------
+# Backward of the hybrid layer
+# ----------------------------------------------------------------------------
+
+
+def hybrid_attention_backward(Q, K, V, dO, modes, cu_seqlens, *, block=64, n_sink=1,
+                              window_blocks=0, keep_fraction=0.2, softmax_scale=0.0):
+    """Gradients of the hybrid layer's output O with respect to Q, K and V for
+    an upstream gradient dO, every head in its routed mode (the FA or SA
+    equation; a head's K/V are shared by its G query heads).
+
+    Per head, with S = scale Q K^T over the visible pairs (others -inf),
+    P = softmax(S) row-wise and O = P V, the chain rule gives
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)), dQ = scale dS K,
+    dK = scale dS^T Q; rowsum(P * dP) = rowsum(dO * O).  dK and dV of a KV head
+    sum over its query heads.  Returns (dQ [T, Hq, d], dK, dV [T, Hkv, d]),
+    float64."""
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = _scale(d, softmax_scale)
+    dQ = np.zeros((T, Hq, d), dtype=np.float64)
+    dK = np.zeros((T, Hkv, d), dtype=np.float64)
+    dV = np.zeros((T, Hkv, d), dtype=np.float64)
+    for b in range(len(cu_seqlens) - 1):
+        s0, e0 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        L = e0 - s0
+        if L <= 0:
+            continue
+        ns, w = sa_geometry(L, block, n_sink, window_blocks, keep_fraction)
+        idx = np.arange(L)
+        for hq in range(Hq):
+            g = hq // G
+            mask = visible(idx[:, None], idx[None, :], int(modes[b, g]), ns, w, block)
+            q = np.asarray(Q[s0:e0, hq], np.float64)
+            k = np.asarray(K[s0:e0, g], np.float64)
+            v = np.asarray(V[s0:e0, g], np.float64)
+            do = np.asarray(dO[s0:e0, hq], np.float64)
+            s = np.where(mask, (q @ k.T) * scale, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = do @ v.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dQ[s0:e0, hq] = scale * (ds @ k)
+            dK[s0:e0, g] += scale * (ds.T @ q)
+            dV[s0:e0, g] += p.T @ do
+    return dQ, dK, dV
 
 
 # ----------------------------------------------------------------------------

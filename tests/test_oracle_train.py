@@ -179,3 +179,96 @@ def test_decode_fa_is_sdpa_over_the_history():
     v = torch.from_numpy(Vh[0]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
     ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[:, 0]
     np.testing.assert_allclose(O[0], ref.numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Backward
+# ----------------------------------------------------------------------------
+
+def _torch_grads(Q, K, V, dO, modes, cu, geom, scale=None):
+    """Reference gradients by torch autograd through an explicitly masked
+    float64 softmax attention, one (sequence, head) at a time."""
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    q = torch.tensor(Q, requires_grad=True)
+    k = torch.tensor(K, requires_grad=True)
+    v = torch.tensor(V, requires_grad=True)
+    outs = []
+    for b in range(len(cu) - 1):
+        s0, e0 = int(cu[b]), int(cu[b + 1])
+        L = e0 - s0
+        if L == 0:
+            continue
+        ns, w = orc.sa_geometry(L, 64, geom.get("n_sink", 1), geom.get("window_blocks", 0),
+                                geom.get("keep_fraction", 0.2))
+        i = torch.arange(L)[:, None]
+        j = torch.arange(L)[None, :]
+        for hq in range(Hq):
+            g = hq // G
+            m = j <= i
+            if modes[b, g]:
+                m = m & ((j // 64 < ns) | (i // 64 - j // 64 < w))
+            sc = (q[s0:e0, hq] @ k[s0:e0, g].T) * scale
+            p = torch.softmax(sc.masked_fill(~m, float("-inf")), dim=-1)
+            o = p @ v[s0:e0, g]
+            outs.append((o * torch.from_numpy(dO[s0:e0, hq])).sum())
+    torch.stack(outs).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def test_backward_matches_autograd():
+    lengths = [150, 0, 333, 64]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    Hq, Hkv, d = 4, 2, 16
+    Q, K, V, dO = _rand(100, T, Hq, d), _rand(101, T, Hkv, d), _rand(102, T, Hkv, d), _rand(103, T, Hq, d)
+    modes = np.array([[0, 1], [1, 0], [1, 1], [0, 1]], np.int8)
+    for geom in (dict(n_sink=1, window_blocks=2), dict(n_sink=0, window_blocks=1),
+                 dict(n_sink=1, keep_fraction=0.3)):
+        got = orc.hybrid_attention_backward(Q, K, V, dO, modes, cu, **geom)
+        ref = _torch_grads(Q, K, V, dO, modes, cu, geom)
+        for a, r in zip(got, ref):
+            np.testing.assert_allclose(a, r, rtol=0, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    L, Hq, Hkv, d = 70, 2, 1, 4
+    cu = np.array([0, L])
+    Q, K, V, dO = _rand(110, L, Hq, d), _rand(111, L, Hkv, d), _rand(112, L, Hkv, d), _rand(113, L, Hq, d)
+    modes = np.array([[1]], np.int8)
+    geom = dict(n_sink=0, window_blocks=1)
+
+    def loss(Qx, Kx, Vx):
+        O, _ = orc.hybrid_attention(Qx, Kx, Vx, modes, cu, **geom)
+        return float((O * dO).sum())
+
+    dQ, dK, dV = orc.hybrid_attention_backward(Q, K, V, dO, modes, cu, **geom)
+    rng = np.random.default_rng(5)
+    eps = 1e-6
+    for arr, grad in ((Q, dQ), (K, dK), (V, dV)):
+        for _ in range(6):
+            ix = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            a = arr.copy()
+            a[ix] += eps
+            up = loss(*(a if x is arr else x for x in (Q, K, V)))
+            a[ix] -= 2 * eps
+            dn = loss(*(a if x is arr else x for x in (Q, K, V)))
+            assert abs((up - dn) / (2 * eps) - grad[ix]) < 1e-6
+
+
+def test_backward_invariants():
+    # a constant shift of K per (sequence, head) leaves O unchanged, so the
+    # keys' gradient sums to zero over the visible keys of every row:
+    # sum_j dS_ij = 0, hence sum over keys of dK = scale * sum_ij dS_ij q_i = 0
+    L, Hq, Hkv, d = 200, 4, 2, 8
+    cu = np.array([0, L])
+    Q, K, V, dO = _rand(120, L, Hq, d), _rand(121, L, Hkv, d), _rand(122, L, Hkv, d), _rand(123, L, Hq, d)
+    for modes in (np.array([[0, 1]], np.int8), np.array([[1, 1]], np.int8)):
+        dQ, dK, dV = orc.hybrid_attention_backward(Q, K, V, dO, modes, cu, n_sink=1,
+                                                   window_blocks=1)
+        np.testing.assert_allclose(dK.sum(axis=0), 0.0, atol=1e-10)
+        # dV sums dO over the queries weighted by probabilities that sum to 1 per row
+        np.testing.assert_allclose(dV.sum(axis=0),
+                                   dO.reshape(L, Hkv, Hq // Hkv, d).sum(axis=(0, 2)), atol=1e-10)
