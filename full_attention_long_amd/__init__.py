@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     ea_dual_prefill,
     ea_dual_prefill_workspace_size,
     ea_gumbel_route,
+    ea_hybrid_backward,
+    ea_hybrid_backward_workspace_size,
     ea_hybrid_prefill,
     ea_hybrid_prefill_plan,
     ea_hybrid_prefill_run,

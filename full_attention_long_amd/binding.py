@@ -100,6 +100,11 @@ def lib() -> ctypes.CDLL:
     L.ea_decode_workspace_size.argtypes = [cd, i32]
     L.ea_decode_step.restype = i32
     L.ea_decode_step.argtypes = [cd, vp, sz, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.ea_hybrid_backward_workspace_size.restype = sz
+    L.ea_hybrid_backward_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.ea_hybrid_backward.restype = i32
+    L.ea_hybrid_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32,
+                                     i32, ctypes.POINTER(SparsityParams), vp, vp, vp, vp, sz, vp]
     L.ea_mfma_probe.restype = i32
     L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
@@ -239,6 +244,39 @@ def ea_hybrid_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace
                                        ctypes.byref(sp), _ptr(out), _ptr(lse), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def ea_hybrid_backward_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype_code):
+    return int(lib().ea_hybrid_backward_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv,
+                                                       head_dim, dtype_code))
+
+
+def ea_hybrid_backward(Q, K, V, O, dO, lse, modes, cu_seqlens, max_seqlen: int, *, n_sink: int = 1,
+                       window_blocks: int = 0, keep_fraction: float = 0.2,
+                       softmax_scale: float = 0.0, block: int = 64, dQ=None, dK=None, dV=None,
+                       workspace=None, stream=None):
+    """(dQ, dK, dV) of the hybrid layer for the upstream gradient dO, given the
+    forward's O and LSE (bf16 tensors; LSE float32 [Hq, T])."""
+    import torch
+    for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (O, "O"), (dO, "dO"), (lse, "lse"),
+                 (modes, "modes"), (cu_seqlens, "cu_seqlens")]:
+        _dev(t, n)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    B = cu_seqlens.numel() - 1
+    code = _dtype_code(Q)
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.empty_like(K) if dK is None else dK
+    dV = torch.empty_like(V) if dV is None else dV
+    if workspace is None:
+        need = ea_hybrid_backward_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    _check(lib().ea_hybrid_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(lse), code,
+                                    _ptr(modes), _ptr(cu_seqlens), B, T, max_seqlen, Hq, Hkv, d,
+                                    ctypes.byref(sp), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dQ, dK, dV
 
 
 def ea_gumbel_route(logits, tau: float, *, gumbel=None, r_soft=None, modes=None,

@@ -401,6 +401,79 @@ ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes,
   return ok();
 }
 
+static size_t bwd_extra_bytes(const ea::Shape& s) {
+  return ((static_cast<size_t>(s.Hq) * s.T * sizeof(float) + 255) & ~static_cast<size_t>(255)) * 2;
+}
+
+size_t ea_hybrid_backward_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                         int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                         ea_dtype dtype) {
+  ea::Shape s;
+  if (check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s) != EA_OK) return 0;
+  g_err.clear();
+  return ea::plan_workspace(s).total + bwd_extra_bytes(s);
+}
+
+ea_status ea_hybrid_backward(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* lse, ea_dtype dtype,
+                             const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                             int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                             int32_t head_dim, const ea_sparsity_params* p, void* dQ, void* dK,
+                             void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  if (dtype != EA_BF16) return fail(EA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
+  ea_status st = check_prefill(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, modes,
+                               cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
+  if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
+  if (!dO || !lse || !dQ || !dK || !dV) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(dO) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return fail(EA_ERR_INVALID_ARG, "dO, dQ, dK and dV must be 16-byte aligned");
+  const size_t need = ws.total + bwd_extra_bytes(s);
+  if (workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (total_tokens == 0) return ok();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "work-list launch failed: %s", hipGetErrorString(e));
+  ea::BwdArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.O = static_cast<const uint16_t*>(O);
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.lse = lse;
+  a.dQ = static_cast<uint16_t*>(dQ);
+  a.dK = static_cast<uint16_t*>(dK);
+  a.dV = static_cast<uint16_t*>(dV);
+  const size_t half = bwd_extra_bytes(s) / 2;
+  a.Dv = reinterpret_cast<float*>(base + ws.total);
+  a.lse2 = reinterpret_cast<float*>(base + ws.total + half);
+  a.cu = cu_seqlens;
+  a.modes = modes;
+  a.seq_w = reinterpret_cast<const int32_t*>(base + ws.seq_w);
+  a.items = reinterpret_cast<const ea::Item*>(base + ws.items_raw);
+  a.order = reinterpret_cast<const int32_t*>(base + ws.order);
+  a.meta = reinterpret_cast<const int32_t*>(base + ws.meta);
+  a.T = s.T;
+  a.max_items = ws.max_items;
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.BMq = s.BMq;
+  a.n_sink = g.n_sink;
+  a.stamp = ea::plan_stamp(s);
+  a.scale = g.scale;
+  const int64_t npair = (static_cast<int64_t>(s.max_seqlen) + 127) / 128;
+  e = ea::launch_backward(s, g, a, npair * s.Hkv * s.B, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ea_status ea_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,
                         int64_t* flops, void* stream) {
   if (!out) return fail(EA_ERR_INVALID_ARG, "null pointer argument");

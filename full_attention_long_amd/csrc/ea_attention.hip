@@ -83,32 +83,6 @@ struct AttnArgs {
   float scale_log2;
 };
 
-// Work-list position of workgroup wg.  The hardware hands workgroup wg to XCD
-// wg mod 8; the j-th workgroup an XCD receives (j = wg / 8) takes entry
-// j mod C of chunk 8 (j / C) + x of the list, C = kXcdChunk, with x = wg mod 8
-// in even rounds j / C and 7 - wg mod 8 in odd ones.  Chunks are cost-sorted,
-// so the snake keeps any XCD from taking the costlier chunk of every round.
-__device__ __forceinline__ int64_t list_position(int64_t wg) {
-  const int64_t j = wg / kNumXcd, round = j / kXcdChunk;
-  const int64_t x = (round & 1) ? (kNumXcd - 1 - wg % kNumXcd) : (wg % kNumXcd);
-  return (round * kNumXcd + x) * kXcdChunk + j % kXcdChunk;
-}
-
-// Whether every row of a tile over query positions [p0, ...] (query blocks
-// [qb0, qb1]) sees every key of block kb, so that the block needs no mask.
-__device__ __forceinline__ bool block_full(int mode, int kb, int p0, int qb0, int qb1, int ns, int w) {
-  if (mode == kModeMiddle) return qb0 - kb >= w;
-  return (kb * kBlock + kBlock - 1 <= p0) && (mode == kModeFA || kb < ns || qb1 - kb < w);
-}
-
-// Whether a row in query block qblk may see block kb at all (the causal test
-// on single keys is applied on top; in the middle set it always holds, since
-// kb <= qblk - w < qblk).
-__device__ __forceinline__ bool block_visible(int mode, int kb, int qblk, int ns, int w) {
-  if (mode == kModeMiddle) return qblk - kb >= w;
-  return mode == kModeFA || kb < ns || qblk - kb < w;
-}
-
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

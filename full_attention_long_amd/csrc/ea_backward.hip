@@ -1,0 +1,435 @@
+// Backward of the hybrid attention layer: dQ, dK and dV for an upstream
+// gradient dO, every head in its routed mode (FA or SA key set), bf16 in and
+// out with float32 accumulation.
+//
+// Pages: the FA and SA equations of the preliminaries and the hybrid-head
+// output equation of "Elastic Attention: Test-time Adaptive Sparsity Ratios
+// for Efficient Transformers"; the router is trained behind a frozen backbone
+// in every layer (training paragraphs), so gradients flow through the
+// attention of each routed head to the layers below.
+//
+// With P = exp(S - LSE) rebuilt from the forward's LSE, and
+// D = rowsum(dO * O) = rowsum(P * dP):
+//   dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dQ = scale dS K,
+//   dK = scale dS^T Q   (dK, dV summed over the G query heads of a KV head).
+// Three kernels: bwd_pre_kernel (D and LSE in log2 units per row),
+// bwd_dq_kernel (query-tile stationary, the forward's work list and K/V
+// tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with 32x32x16 MFMAs)
+// and bwd_dkv_kernel (key stationary: each wave owns 16 keys of its KV head
+// and walks the query blocks that can see them, head by head: S = Q K^T,
+// dP = dO V^T, dV += P^T dO, dK += dS^T Q with 16x16x32 MFMAs).
+#include "ea_internal.h"
+
+#include <math.h>
+
+namespace ea {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i16x4 ds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 tr_pair(const uint16_t* lo, const uint16_t* hi) {
+  const i16x4 a = ds_read_tr(lo), b = ds_read_tr(hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// D[hq, t] = sum_d dO * O and LSE in log2 units, per (token, query head) row;
+// the d / 8 threads of a row sit in one wave.
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ lse, int64_t T,
+                                                      int32_t Hq, int32_t d, float* __restrict__ Dv,
+                                                      float* __restrict__ lse2) {
+  const int cpr = d / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = i / cpr;
+  const bool ok = row < T * Hq;
+  float acc = 0.f;
+  if (ok) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(O + i * 8);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + i * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += static_cast<float>(a[e]) * static_cast<float>(b[e]);
+  }
+  for (int off = cpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (ok && i % cpr == 0) {
+    const int64_t t = row / Hq;
+    const int hq = static_cast<int>(row - t * Hq);
+    Dv[static_cast<int64_t>(hq) * T + t] = acc;
+    lse2[static_cast<int64_t>(hq) * T + t] = lse[static_cast<int64_t>(hq) * T + t] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one work item (the forward's query tile of 256 rows, 32 per wave) over
+// its visible key blocks.  Per block: K in the row layout (S^T = K Q^T) and in
+// the transposing layout (dQ^T += K^T dS^T), V in the row layout
+// (dP^T = V dO^T), all three by direct buffer-to-LDS loads one block ahead.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int CPR = D / 8;
+  constexpr int TILE = kBlock * D;
+  constexpr int RPI = 1024 / (2 * D);
+  constexpr int NDMA = kBlock / RPI / kAttnWaves;
+  constexpr int DT = D / 32;
+  constexpr int NQ = D / 16;
+  constexpr int KGS = RPI * D + 32;
+  constexpr int KTILE = (kBlock / RPI) * KGS;
+  constexpr int VSW = (CPR / 4) - 1;
+  auto kfold = [](int j) { return D == 128 ? j : (j >> 1); };
+  __shared__ __attribute__((aligned(1024))) uint16_t Kr0[KTILE], Kr1[KTILE], Vr0[KTILE], Vr1[KTILE],
+      Kt0[TILE], Kt1[TILE];
+
+  const int64_t pos_in_list = list_position(blockIdx.x);
+  if (a.meta[kMetaStamp] != a.stamp) return;
+  if (pos_in_list >= static_cast<int64_t>(a.meta[kMetaTiles]) * a.Hkv) return;
+  const Item it = a.items[a.order[pos_in_list]];
+  const int b = it.b, kvh = it.kvh, mode = it.mode;
+  const int tok0 = a.cu[b];
+  const int L = a.cu[b + 1] - tok0;
+  const int ns = a.n_sink, w = a.seq_w[b];
+  const int p0 = it.qt * a.BMq;
+  const int p1 = min(p0 + a.BMq, L) - 1;
+  const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
+  const KeyRange kr = key_range(mode, qb0, qb1, ns, w);
+  const int nblk = kr.count();
+  auto kb_of = [&](int n) { return n < kr.r1_end ? n : kr.r2_beg + (n - kr.r1_end); };
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, h = lane / 32, lq = lane % 32;
+  const int row = wave * 32 + lq;
+  const int hh = row / a.BMq;
+  const int pos = p0 + row % a.BMq;
+  const bool rvalid = hh < a.G && pos < L;
+  const int hq = kvh * a.G + hh;
+  const int qblk = pos / kBlock;
+
+  bf16x8 qf[NQ], of[NQ];
+  {
+    const int64_t r = (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      qf[u] = rvalid ? *reinterpret_cast<const bf16x8*>(a.Q + r + 16 * u + 8 * h) : bf16x8{};
+      of[u] = rvalid ? *reinterpret_cast<const bf16x8*>(a.dO + r + 16 * u + 8 * h) : bf16x8{};
+    }
+  }
+  const int64_t li = static_cast<int64_t>(hq) * a.T + tok0 + pos;
+  const float lrow = rvalid ? a.lse2[li] : INFINITY;  // an invalid row's P is 0
+  const float drow = rvalid ? a.Dv[li] : 0.f;
+  const float c = a.scale * kLog2e;
+
+  const int rs = a.Hkv * D;
+  const uint16_t* Kseq = a.K + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
+  const uint16_t* Vseq = a.V + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
+  int dma_roff[NDMA], dma_toff[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = (wave * NDMA + i) * RPI + lane / CPR;
+    dma_roff[i] = (r * rs + ((lane % CPR) ^ kfold(lane / CPR)) * 8) * 2;
+    dma_toff[i] = (r * rs + ((lane % CPR) ^ (4 * ((r & 3) & VSW))) * 8) * 2;
+  }
+  auto dma = [&](const uint16_t* seq, const int* off, uint16_t* tile, int gstride, int kb) {
+    const int key0 = kb * kBlock;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(seq + static_cast<int64_t>(key0) * rs), 0,
+        static_cast<unsigned>(L - key0) * static_cast<unsigned>(rs) * 2u, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(tile + (wave * NDMA + i) * gstride), 16,
+          off[i], 0, 0, 0);
+  };
+  int koff_e, koff_o;
+  {
+    const int j = lq % RPI, f = kfold(j), bb = f >> 1, e = f & 1;
+    const int base = (lq / RPI) * KGS + j * D + (h ^ e) * 8;
+    koff_e = base + 16 * bb;
+    koff_o = base - 16 * bb;
+  }
+  int toff[DT];
+  {
+    const int vr = 4 * h + (lane & 15) / 4;
+    const int clow = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int j = ((lane >> 2) & 3) & VSW;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) toff[t] = vr * D + (4 * (t ^ j) + clow) * 8 + 4 * (lane & 1);
+  }
+  // A-operand rows of a row-layout tile times the B fragments
+  auto rowmm = [&](const uint16_t* tile, const bf16x8* bf, f32x16& x0, f32x16& x1) {
+    x0 = f32x16{};
+    x1 = f32x16{};
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int o0 = ((u & 1) ? koff_o : koff_e) + 16 * u;
+      x0 = mfma32(*reinterpret_cast<const bf16x8*>(tile + o0), bf[u], x0);
+      x1 = mfma32(*reinterpret_cast<const bf16x8*>(tile + o0 + (32 / RPI) * KGS), bf[u], x1);
+    }
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) dq[t] = f32x16{};
+
+  auto block = [&](int kb, const uint16_t* kr_, const uint16_t* vr_, const uint16_t* kt_) {
+    f32x16 s0, s1, p0v, p1v;
+    rowmm(kr_, qf, s0, s1);
+    const bool full = block_full(mode, kb, p0, qb0, qb1, ns, w);
+    const bool blk_ok = block_visible(mode, kb, qblk, ns, w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
+      const bool v0 = full || (blk_ok && j <= pos), v1 = full || (blk_ok && j + 32 <= pos);
+      s0[i] = v0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -lrow)) : 0.f;
+      s1[i] = v1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lrow)) : 0.f;
+    }
+    rowmm(vr_, of, p0v, p1v);  // dP^T
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x8 t;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 8 * (q & 1) + e;
+        t[e] = q < 2 ? s0[k] * (p0v[k] - drow) : s1[k] * (p1v[k] - drow);
+      }
+      dsb[q] = __builtin_convertvector(t, bf16x8);
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dq[t] = mfma32(tr_pair(kt_ + toff[t] + 16 * u * D, kt_ + toff[t] + (16 * u + 8) * D),
+                       dsb[u], dq[t]);
+  };
+
+  if (nblk > 0) {
+    dma(Kseq, dma_roff, Kr0, KGS, kb_of(0));
+    dma(Vseq, dma_roff, Vr0, KGS, kb_of(0));
+    dma(Kseq, dma_toff, Kt0, RPI * D, kb_of(0));
+    __syncthreads();
+    for (int n = 0; n < nblk; n += 2) {
+      const int nx = kb_of(min(n + 1, nblk - 1));
+      dma(Kseq, dma_roff, Kr1, KGS, nx);
+      dma(Vseq, dma_roff, Vr1, KGS, nx);
+      dma(Kseq, dma_toff, Kt1, RPI * D, nx);
+      block(kb_of(n), Kr0, Vr0, Kt0);
+      __syncthreads();
+      if (n + 1 < nblk) {
+        const int nx2 = kb_of(min(n + 2, nblk - 1));
+        dma(Kseq, dma_roff, Kr0, KGS, nx2);
+        dma(Vseq, dma_roff, Vr0, KGS, nx2);
+        dma(Kseq, dma_toff, Kt0, RPI * D, nx2);
+        block(kb_of(n + 1), Kr1, Vr1, Kt1);
+        __syncthreads();
+      }
+    }
+  }
+
+  if (rvalid) {
+    uint16_t* dst = a.dQ + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dq[t][4 * q + e] * a.scale;
+        *reinterpret_cast<bf16x4*>(dst + 32 * t + 8 * q + 4 * h) = __builtin_convertvector(v, bf16x4);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: a workgroup owns 128 keys (two key blocks) of one KV head of one
+// sequence, 16 per wave, and walks the query blocks that can see them; for
+// each query block and each of the G query heads it stages that head's Q and
+// dO rows, LSE and D in LDS (the next stage prefetched into registers).
+// ---------------------------------------------------------------------------
+constexpr int kDkvKeys = 128;
+
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int NU = D / 32;    // 32-wide d steps
+  constexpr int NM = D / 16;    // 16-wide d tiles of dK, dV
+  constexpr int QROW = D + 16;  // padded LDS rows of the Q and dO tiles
+  constexpr int NCH = kBlock * D / 8 / 512;  // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBlock * QROW], Os[kBlock * QROW];
+  __shared__ __attribute__((aligned(16))) float Ls[kBlock], Ds[kBlock];
+
+  const int64_t item = blockIdx.x;
+  const int b = static_cast<int>(item % a.B);
+  const int64_t rest = item / a.B;
+  const int g = static_cast<int>(rest % a.Hkv);
+  const int pair = static_cast<int>(rest / a.Hkv);
+  const int tok0 = a.cu[b];
+  const int L = a.cu[b + 1] - tok0;
+  if (pair * kDkvKeys >= L) return;
+  const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + g] != 0 ? kModeSA : kModeFA;
+  const int ns = a.n_sink, w = a.seq_w[b];
+  const int N = (L + kBlock - 1) / kBlock;
+  const int kb0 = 2 * pair;
+  const int qb_lo = kb0;
+  const int qb_hi = (mode == kModeSA && kb0 >= ns) ? min(N - 1, kb0 + w) : N - 1;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, lg = lane / 16, li = lane % 16;
+  const int key_b = pair * kDkvKeys + wave * 16 + li;  // this lane's key as a B column
+  const int kbj = key_b / kBlock;
+  // K and V rows as the B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kf[NU], vf[NU];
+  {
+    const bool kv = key_b < L;
+    const int64_t r = (static_cast<int64_t>(tok0 + (kv ? key_b : 0)) * a.Hkv + g) * D;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      kf[u] = kv ? *reinterpret_cast<const bf16x8*>(a.K + r + 32 * u + 8 * lg) : bf16x8{};
+      vf[u] = kv ? *reinterpret_cast<const bf16x8*>(a.V + r + 32 * u + 8 * lg) : bf16x8{};
+    }
+  }
+  f32x4 dk[NM], dv[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    dk[m] = f32x4{};
+    dv[m] = f32x4{};
+  }
+  const float c = a.scale * kLog2e;
+
+  // stage (qb, hh) -> registers
+  u32x4 qreg[NCH], oreg[NCH];
+  float lreg = 0.f, dreg = 0.f;
+  auto fetch = [&](int qb, int hh) {
+    const int hq = g * a.G + hh;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int ci = k * 512 + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int p = qb * kBlock + r;
+      const int64_t src = (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + col;
+      qreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
+      oreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.dO + src) : u32x4{0, 0, 0, 0};
+    }
+    if (tid < kBlock) {
+      const int p = qb * kBlock + tid;
+      const int64_t ix = static_cast<int64_t>(hq) * a.T + tok0 + p;
+      lreg = p < L ? a.lse2[ix] : INFINITY;
+      dreg = p < L ? a.Dv[ix] : 0.f;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int ci = k * 512 + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Qs + r * QROW + col) = qreg[k];
+      *reinterpret_cast<u32x4*>(Os + r * QROW + col) = oreg[k];
+    }
+    if (tid < kBlock) {
+      Ls[tid] = lreg;
+      Ds[tid] = dreg;
+    }
+  };
+
+  const int nsteps = (qb_hi - qb_lo + 1) * a.G;
+  fetch(qb_lo, 0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int qb = qb_lo + st / a.G;
+    __syncthreads();  // the previous step's reads of the tiles are done
+    stage();
+    __syncthreads();
+    if (st + 1 < nsteps) fetch(qb_lo + (st + 1) / a.G, (st + 1) % a.G);
+
+    // S and dP: 4 query tiles of 16 rows; lane holds key li, rows 16 qt + 4 lg + i
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      s[qt] = f32x4{};
+      dp[qt] = f32x4{};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int off = (16 * qt + li) * QROW + 32 * u + 8 * lg;
+        s[qt] = mfma16(*reinterpret_cast<const bf16x8*>(Qs + off), kf[u], s[qt]);
+        dp[qt] = mfma16(*reinterpret_cast<const bf16x8*>(Os + off), vf[u], dp[qt]);
+      }
+    }
+    // P and dS (as bf16 A operands: keys x 32 queries per pair of tiles)
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * qt + 4 * lg);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * qt + 4 * lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = qb * kBlock + 16 * qt + 4 * lg + i;
+        const bool vis = key_b <= p && p < L &&
+                         (mode == kModeFA || kbj < ns || p / kBlock - kbj < w);
+        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][i], c, -lv[i])) : 0.f;
+        pa[qt / 2][4 * (qt & 1) + i] = static_cast<__bf16>(pv);
+        da[qt / 2][4 * (qt & 1) + i] = static_cast<__bf16>(pv * (dp[qt][i] - dv4[i]));
+      }
+    }
+    // dV += P^T dO, dK += dS^T Q: B from the tiles by transposing reads, query
+    // rows 32 p2 + 4 lg + 0..3 and + 16, the order pa / da hold them in
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int off = (32 * p2 + 4 * lg + li / 4) * QROW + 16 * m + 4 * (li & 3);
+        dv[m] = mfma16(pa[p2], tr_pair(Os + off, Os + off + 16 * QROW), dv[m]);
+        dk[m] = mfma16(da[p2], tr_pair(Qs + off, Qs + off + 16 * QROW), dk[m]);
+      }
+  }
+
+  // lane holds keys wave 16 + 4 lg + i, dims 16 m + li
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = pair * kDkvKeys + wave * 16 + 4 * lg + i;
+    if (key >= L) continue;
+    const int64_t r = (static_cast<int64_t>(tok0 + key) * a.Hkv + g) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      a.dK[r + 16 * m + li] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dk[m][i] * a.scale));
+      a.dV[r + 16 * m + li] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dv[m][i]));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Shape& s, const Geometry& g, const BwdArgs& args,
+                           const int64_t dkv_items, hipStream_t st) {
+  const int64_t rows = s.T * s.Hq * (s.d / 8);
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, st,
+                     args.O, args.dO, args.lse, s.T, s.Hq, s.d, args.Dv, args.lse2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
+  const unsigned grid = static_cast<unsigned>((args.max_items + span - 1) / span * span);
+  if (s.d == 128) {
+    hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128>), dim3(static_cast<unsigned>(dkv_items)), dim3(512), 0, st, args);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64>), dim3(static_cast<unsigned>(dkv_items)), dim3(512), 0, st, args);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ea

@@ -64,6 +64,32 @@ __host__ __device__ inline KeyRange key_range(int mode, int qb0, int qb1, int n_
   return r;
 }
 
+// Work-list position of workgroup wg.  The hardware hands workgroup wg to XCD
+// wg mod 8; the j-th workgroup an XCD receives (j = wg / 8) takes entry
+// j mod C of chunk 8 (j / C) + x of the list, C = kXcdChunk, with x = wg mod 8
+// in even rounds j / C and 7 - wg mod 8 in odd ones.  Chunks are cost-sorted,
+// so the snake keeps any XCD from taking the costlier chunk of every round.
+__device__ inline int64_t list_position(int64_t wg) {
+  const int64_t j = wg / kNumXcd, round = j / kXcdChunk;
+  const int64_t x = (round & 1) ? (kNumXcd - 1 - wg % kNumXcd) : (wg % kNumXcd);
+  return (round * kNumXcd + x) * kXcdChunk + j % kXcdChunk;
+}
+
+// Whether every row of a tile over query positions [p0, ...] (query blocks
+// [qb0, qb1]) sees every key of block kb, so that the block needs no mask.
+__device__ inline bool block_full(int mode, int kb, int p0, int qb0, int qb1, int ns, int w) {
+  if (mode == kModeMiddle) return qb0 - kb >= w;
+  return (kb * kBlock + kBlock - 1 <= p0) && (mode == kModeFA || kb < ns || qb1 - kb < w);
+}
+
+// Whether a row in query block qblk may see block kb at all (the causal test
+// on single keys is applied on top; in the middle set it always holds, since
+// kb <= qblk - w < qblk).
+__device__ inline bool block_visible(int mode, int kb, int qblk, int ns, int w) {
+  if (mode == kModeMiddle) return qblk - kb >= w;
+  return mode == kModeFA || kb < ns || qblk - kb < w;
+}
+
 // Slots of the small int32 header at the start of the workspace.
 enum Meta : int {
   kMetaTiles = 0,       // sum over sequences of ceil(L_b / BMq); items = tiles * Hkv
@@ -178,6 +204,33 @@ hipError_t launch_cache_fill(const CacheView& c, const int32_t* cu, int64_t T, c
                              const void* V, hipStream_t st);
 hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, const void* k_new,
                          const void* v_new, hipStream_t st);
+
+// Arguments of the backward kernels (ea_backward.hip).
+struct BwdArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* O;
+  const uint16_t* dO;
+  const float* lse;     // [Hq, T] natural log, from the forward
+  uint16_t* dQ;
+  uint16_t* dK;
+  uint16_t* dV;
+  float* Dv;            // [Hq, T] rowsum(dO * O) (workspace)
+  float* lse2;          // [Hq, T] LSE in log2 units (workspace)
+  const int32_t* cu;
+  const int8_t* modes;
+  const int32_t* seq_w;
+  const Item* items;
+  const int32_t* order;
+  const int32_t* meta;
+  int64_t T, max_items;
+  int32_t B, Hq, Hkv, G, BMq, n_sink, stamp;
+  float scale;
+};
+
+hipError_t launch_backward(const Shape& s, const Geometry& g, const BwdArgs& args,
+                           const int64_t dkv_items, hipStream_t st);
 
 // Training-forward helpers (ea_dual.hip).
 hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float tau, int64_t n,

@@ -240,6 +240,37 @@ ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype 
                           void* O_fa, void* O_sa, float* lse_fa, float* lse_sa, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace ea_hybrid_backward needs (0 if the sizes are
+ * invalid): the forward's work list plus two float32 [Hq, T] arrays. */
+size_t ea_hybrid_backward_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                         int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                         ea_dtype dtype);
+
+/* ea_hybrid_backward - gradients of the hybrid layer for an upstream dO.
+ *
+ * The router is trained behind a frozen backbone in every layer (paper body:
+ * training paragraphs), so a layer's backward must carry gradients through
+ * its routed attention: with P = softmax(scale Q K^T) over each head's
+ * visible keys and O = P V,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV of a KV head summed over its query heads.
+ *
+ *   Q, K, V, modes, cu_seqlens, sizes, params: as for ea_hybrid_prefill
+ *   O, lse     the forward's outputs for these inputs (lse required)
+ *   dO         [T, Hq, head_dim] upstream gradient
+ *   dQ         out [T, Hq, head_dim]; dK, dV out [T, Hkv, head_dim]
+ * bf16 only (float32 accumulation); every output row is written once, by one
+ * workgroup, with no atomics (bitwise reproducible).  Other limits and errors
+ * are those of ea_hybrid_prefill. */
+ea_status ea_hybrid_backward(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* lse, ea_dtype dtype,
+                             const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                             int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                             int32_t head_dim, const ea_sparsity_params* params, void* dQ,
+                             void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* ---- Decode with a mode-aware KV cache -------------------------------------
  *
  * One new token per sequence attends to its cached keys with the prefill's

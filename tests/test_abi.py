@@ -19,7 +19,8 @@ def test_every_header_function_is_exported():
                           "ea_hybrid_prefill_plan", "ea_hybrid_prefill_run", "ea_mfma_probe",
                           "ea_gumbel_route", "ea_dual_prefill_workspace_size", "ea_dual_prefill",
                           "ea_kvcache_bytes", "ea_kvcache_init", "ea_kvcache_prefill",
-                          "ea_decode_workspace_size", "ea_decode_step"}
+                          "ea_decode_workspace_size", "ea_decode_step",
+                          "ea_hybrid_backward_workspace_size", "ea_hybrid_backward"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -267,3 +268,22 @@ def test_kvcache_and_decode_host_errors():
     assert step(ws_bytes=16) == -3
     assert step(q=A + 8) == -1 and "16-byte" in ea.ea_last_error()
     assert step(d_=_desc(head_dim=80)) == -2
+
+
+def test_backward_host_errors():
+    L = ea.lib()
+    sp = bnd.SparsityParams(64, 1, 0, 0.2, 0.0)
+    A = FAKE
+    ws = ea.ea_hybrid_backward_workspace_size(1, 1000, 1000, 8, 2, 128, bnd.EA_BF16)
+    assert ws > ea.ea_hybrid_prefill_workspace_size(1, 1000, 1000, 8, 2, 128, bnd.EA_BF16) + 2 * 8 * 1000 * 4 - 1
+
+    def call(dtype=1, dO=A, lse=A, dQ=A, ws_bytes=ws, O=A):
+        return L.ea_hybrid_backward(A, A, A, O, dO, lse, dtype, A, A, 1, 1000, 1000, 8, 2, 128,
+                                    ctypes.byref(sp), dQ, A, A, A, ws_bytes, None)
+
+    assert call(dtype=0) == -2 and "bf16" in ea.ea_last_error()
+    assert call(dO=None) == -1
+    assert call(lse=None) == -1
+    assert call(O=None) == -1
+    assert call(dQ=A + 8) == -1 and "16-byte" in ea.ea_last_error()
+    assert call(ws_bytes=ws - 1) == -3
