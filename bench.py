@@ -413,6 +413,72 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_backward(args):
+    """Backward of each --runs layer (work list, D / LSE pass, dQ kernel, dK/dV
+    kernel) after its forward; effective FLOPs = 2.5x the forward's (the five
+    products S, dP, dV, dQ, dK over the visible blocks).  Prints one JSON line
+    of its own."""
+    import torch
+
+    import full_attention_long_amd as ea
+    from full_attention_long_amd import metrics
+    runs = []
+    tot_ef = tot_ms = 0.0
+    for name in args.runs.split(","):
+        ly = Layer(name)
+        c = ly.case
+        ly.step()
+        torch.cuda.synchronize()
+        g = torch.Generator(device="cuda").manual_seed(3)
+        dO = torch.randn(ly.q.shape, generator=g, device="cuda").to(torch.bfloat16)
+        dQ, dK, dV = torch.empty_like(ly.q), torch.empty_like(ly.k), torch.empty_like(ly.v)
+        nbytes = ea.ea_hybrid_backward_workspace_size(c.B, c.T, ly.maxlen, c.Hq, c.Hkv, c.d, 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+        def bwd():
+            ea.ea_hybrid_backward(ly.q, ly.k, ly.v, ly.O, dO, ly.lse, ly.modes, ly.cu, ly.maxlen,
+                                  dQ=dQ, dK=dK, dV=dV, workspace=ws, **ly.geom)
+
+        for _ in range(args.warmup):
+            bwd()
+        torch.cuda.synchronize()
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        evs = [(E(), E()) for _ in range(args.steps)]
+        for s in range(args.steps):
+            evs[s][0].record()
+            bwd()
+            evs[s][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        ef = 2.5 * metrics.effective_flops(ly.modes.cpu().numpy(), c.lengths, c.Hq, c.Hkv, c.d,
+                                           n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+        log(f"backward {name}: {ms:.3f} ms, {ef / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        runs.append({"workload": name, "backward_ms": round(ms, 4), "effective_flops": int(ef),
+                     "tflops": round(ef / (ms * 1e-3) / 1e12, 3),
+                     "sa_kv_heads": int(ly.modes.sum().item())})
+        tot_ef += ef
+        tot_ms += ms
+        del ly, dO, dQ, dK, dV, ws
+        torch.cuda.empty_cache()
+    value = tot_ef / (tot_ms * 1e-3) / 1e12
+    probe = mfma_probe()
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
+    out = {
+        "metric": "hybrid-layer backward effective TFLOP/s at 128K (2.5x forward FLOPs)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(tot_ms / len(runs), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "+".join(r["workload"] for r in runs) + ":backward", "runs": runs},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(value / peak, 4), "traffic": None,
+                     "kernel": "ea_hybrid_backward (bwd_pre + bwd_dq_kernel + bwd_dkv_kernel)",
+                     "mfma_loop_tflops": probe["tflops"],
+                     "frac_of_mfma_loop": round(value / probe["tflops"], 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calibrate(mib):
     """One elementwise kernel of known traffic (reads and writes mib MiB), so
     that profiler byte counters can be scaled to bytes."""
@@ -475,6 +541,8 @@ def main():
                     help="measure the dual-mode (training) forward of the first --runs workload "
                          "instead (default qwen4b_s128k_sa6)")
     ap.add_argument("--tau", type=float, default=1.0, help="Gumbel-Softmax temperature (--dual)")
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the hybrid-layer backward of each --runs workload instead")
     ap.add_argument("--decode", action="store_true",
                     help="measure decode steps over a mode-aware KV cache holding each --runs "
                          "workload as the prompt instead (default qwen4b_s128k_sa2,sa6 and "
@@ -502,6 +570,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_mib:
         calibrate(args.calibrate_mib)
+    if args.backward:
+        bench_backward(args)
+        return
     if args.decode:
         if args.runs == ",".join(DEFAULT_RUNS):
             args.runs = "qwen4b_s128k_sa2,qwen4b_s128k_sa6,varlen8"

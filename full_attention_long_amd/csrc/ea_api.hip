@@ -401,8 +401,11 @@ ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes,
   return ok();
 }
 
+static size_t bwd_row_bytes(const ea::Shape& s) {
+  return (static_cast<size_t>(s.Hq) * s.T * sizeof(float) + 255) & ~static_cast<size_t>(255);
+}
 static size_t bwd_extra_bytes(const ea::Shape& s) {
-  return ((static_cast<size_t>(s.Hq) * s.T * sizeof(float) + 255) & ~static_cast<size_t>(255)) * 2;
+  return 2 * bwd_row_bytes(s) + ea::dkv_list_layout(s).total;
 }
 
 size_t ea_hybrid_backward_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
@@ -449,9 +452,9 @@ ea_status ea_hybrid_backward(const void* Q, const void* K, const void* V, const 
   a.dQ = static_cast<uint16_t*>(dQ);
   a.dK = static_cast<uint16_t*>(dK);
   a.dV = static_cast<uint16_t*>(dV);
-  const size_t half = bwd_extra_bytes(s) / 2;
+  const size_t rb = bwd_row_bytes(s);
   a.Dv = reinterpret_cast<float*>(base + ws.total);
-  a.lse2 = reinterpret_cast<float*>(base + ws.total + half);
+  a.lse2 = reinterpret_cast<float*>(base + ws.total + rb);
   a.cu = cu_seqlens;
   a.modes = modes;
   a.seq_w = reinterpret_cast<const int32_t*>(base + ws.seq_w);
@@ -468,8 +471,7 @@ ea_status ea_hybrid_backward(const void* Q, const void* K, const void* V, const 
   a.n_sink = g.n_sink;
   a.stamp = ea::plan_stamp(s);
   a.scale = g.scale;
-  const int64_t npair = (static_cast<int64_t>(s.max_seqlen) + 127) / 128;
-  e = ea::launch_backward(s, g, a, npair * s.Hkv * s.B, hs);
+  e = ea::launch_backward(s, g, a, ea::dkv_list_layout(s), base + ws.total + 2 * rb, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -22,6 +22,8 @@
 
 #include <math.h>
 
+#include <hipcub/hipcub.hpp>
+
 namespace ea {
 namespace {
 
@@ -260,36 +262,39 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: a workgroup owns 128 keys (two key blocks) of one KV head of one
-// sequence, 16 per wave, and walks the query blocks that can see them; for
+// dK, dV: a workgroup owns kDkvKeys keys of one KV head of one sequence, 16
+// per wave, and walks the query blocks that can see them; for
 // each query block and each of the G query heads it stages that head's Q and
 // dO rows, LSE and D in LDS (the next stage prefetched into registers).
 // ---------------------------------------------------------------------------
-constexpr int kDkvKeys = 128;
+constexpr int kDkvThreads = 64 * kDkvWaves;
 
 template <int D>
-__global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int NU = D / 32;    // 32-wide d steps
   constexpr int NM = D / 16;    // 16-wide d tiles of dK, dV
   constexpr int QROW = D + 16;  // padded LDS rows of the Q and dO tiles
-  constexpr int NCH = kBlock * D / 8 / 512;  // 16-byte chunks per thread per tile
+  constexpr int NCH = kBlock * D / 8 / kDkvThreads;  // 16-byte chunks per thread per tile
+  static_assert(NCH * kDkvThreads * 8 == kBlock * D, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t Qs[kBlock * QROW], Os[kBlock * QROW];
   __shared__ __attribute__((aligned(16))) float Ls[kBlock], Ds[kBlock];
 
-  const int64_t item = blockIdx.x;
-  const int b = static_cast<int>(item % a.B);
-  const int64_t rest = item / a.B;
+  // raw item ((b Hkv + g) npair + pair), taken in the list's cost order
+  const int64_t item = a.dkv_order[blockIdx.x];
+  const int pair = static_cast<int>(item % a.npair);
+  const int64_t rest = item / a.npair;
   const int g = static_cast<int>(rest % a.Hkv);
-  const int pair = static_cast<int>(rest / a.Hkv);
+  const int b = static_cast<int>(rest / a.Hkv);
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
   if (pair * kDkvKeys >= L) return;
   const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + g] != 0 ? kModeSA : kModeFA;
   const int ns = a.n_sink, w = a.seq_w[b];
   const int N = (L + kBlock - 1) / kBlock;
-  const int kb0 = 2 * pair;
+  const int kb0 = pair * (kDkvKeys / kBlock);
+  const int kb1 = min(N - 1, kb0 + kDkvKeys / kBlock - 1);
   const int qb_lo = kb0;
-  const int qb_hi = (mode == kModeSA && kb0 >= ns) ? min(N - 1, kb0 + w) : N - 1;
+  const int qb_hi = (mode == kModeSA && kb0 >= ns) ? min(N - 1, kb1 + w - 1) : N - 1;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, lg = lane / 16, li = lane % 16;
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a) {
     const int hq = g * a.G + hh;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const int ci = k * 512 + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
       const int p = qb * kBlock + r;
       const int64_t src = (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + col;
       qreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a) {
   auto stage = [&]() {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const int ci = k * 512 + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
       *reinterpret_cast<u32x4*>(Qs + r * QROW + col) = qreg[k];
       *reinterpret_cast<u32x4*>(Os + r * QROW + col) = oreg[k];
     }
@@ -411,10 +416,82 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
+// Cost (query blocks walked) of every dK/dV item, as a sort key: most
+// expensive first in bands of 2^kCostBandShift blocks, empty items last.
+__global__ __launch_bounds__(256) void dkv_items_kernel(BwdArgs a, int32_t maxcost,
+                                                        uint32_t* __restrict__ keys,
+                                                        int32_t* __restrict__ vals) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (x >= a.dkv_n) return;
+  vals[x] = static_cast<int32_t>(x);
+  const int pair = static_cast<int>(x % a.npair);
+  const int64_t rest = x / a.npair;
+  const int g = static_cast<int>(rest % a.Hkv);
+  const int b = static_cast<int>(rest / a.Hkv);
+  const int L = a.cu[b + 1] - a.cu[b];
+  const uint32_t last = static_cast<uint32_t>(maxcost >> kCostBandShift) + 1;
+  if (pair * kDkvKeys >= L) {
+    keys[x] = last;
+    return;
+  }
+  const int N = (L + kBlock - 1) / kBlock;
+  const int kb0 = pair * (kDkvKeys / kBlock);
+  const int kb1 = min(N - 1, kb0 + kDkvKeys / kBlock - 1);
+  const bool sa = a.modes[static_cast<int64_t>(b) * a.Hkv + g] != 0;
+  const int qb_hi = (sa && kb0 >= a.n_sink) ? min(N - 1, kb1 + a.seq_w[b] - 1) : N - 1;
+  const int cost = qb_hi - kb0 + 1;
+  keys[x] = static_cast<uint32_t>((maxcost - min(cost, maxcost)) >> kCostBandShift);
+}
+
+int bits_for(uint32_t max_value) {
+  int bits = 1;
+  while ((int64_t(1) << bits) <= max_value) ++bits;
+  return bits;
+}
+
 }  // namespace
 
-hipError_t launch_backward(const Shape& s, const Geometry& g, const BwdArgs& args,
-                           const int64_t dkv_items, hipStream_t st) {
+DkvList dkv_list_layout(const Shape& s) {
+  auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  DkvList l{};
+  l.npair = static_cast<int32_t>((static_cast<int64_t>(s.max_seqlen) + kDkvKeys - 1) / kDkvKeys);
+  l.n = static_cast<int64_t>(s.B) * s.Hkv * l.npair;
+  l.maxcost = (s.max_seqlen + kBlock - 1) / kBlock;
+  size_t tmp = 0;
+  if (hipcub::DeviceRadixSort::SortPairs(
+          nullptr, tmp, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
+          static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr), static_cast<int>(l.n), 0,
+          bits_for(static_cast<uint32_t>(l.maxcost >> kCostBandShift) + 1),
+          static_cast<hipStream_t>(nullptr)) != hipSuccess)
+    tmp = 0;
+  size_t off = 0;
+  l.keys_in = off;  off = align(off + sizeof(uint32_t) * l.n);
+  l.keys_out = off; off = align(off + sizeof(uint32_t) * l.n);
+  l.vals_in = off;  off = align(off + sizeof(int32_t) * l.n);
+  l.order = off;    off = align(off + sizeof(int32_t) * l.n);
+  l.sort_tmp = off; off = align(off + tmp);
+  l.sort_tmp_bytes = tmp;
+  l.total = off;
+  return l;
+}
+
+hipError_t launch_backward(const Shape& s, const Geometry& g, BwdArgs args, const DkvList& l,
+                           char* list_base, hipStream_t st) {
+  uint32_t* keys_in = reinterpret_cast<uint32_t*>(list_base + l.keys_in);
+  uint32_t* keys_out = reinterpret_cast<uint32_t*>(list_base + l.keys_out);
+  int32_t* vals_in = reinterpret_cast<int32_t*>(list_base + l.vals_in);
+  int32_t* order = reinterpret_cast<int32_t*>(list_base + l.order);
+  args.dkv_order = order;
+  args.dkv_n = l.n;
+  args.npair = l.npair;
+  hipLaunchKernelGGL(dkv_items_kernel, dim3(static_cast<unsigned>((l.n + 255) / 256)), dim3(256), 0,
+                     st, args, l.maxcost, keys_in, vals_in);
+  size_t tmp_bytes = l.sort_tmp_bytes;
+  hipError_t e0 = hipcub::DeviceRadixSort::SortPairs(
+      list_base + l.sort_tmp, tmp_bytes, keys_in, keys_out, vals_in, order, static_cast<int>(l.n), 0,
+      bits_for(static_cast<uint32_t>(l.maxcost >> kCostBandShift) + 1), st);
+  if (e0 != hipSuccess) return e0;
+  const int64_t dkv_items = l.n;
   const int64_t rows = s.T * s.Hq * (s.d / 8);
   hipLaunchKernelGGL(bwd_pre_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, st,
                      args.O, args.dO, args.lse, s.T, s.Hq, s.d, args.Dv, args.lse2);
@@ -424,10 +501,10 @@ hipError_t launch_backward(const Shape& s, const Geometry& g, const BwdArgs& arg
   const unsigned grid = static_cast<unsigned>((args.max_items + span - 1) / span * span);
   if (s.d == 128) {
     hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<128>), dim3(static_cast<unsigned>(dkv_items)), dim3(512), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128>), dim3(static_cast<unsigned>(dkv_items)), dim3(kDkvThreads), 0, st, args);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<64>), dim3(static_cast<unsigned>(dkv_items)), dim3(512), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64>), dim3(static_cast<unsigned>(dkv_items)), dim3(kDkvThreads), 0, st, args);
   }
   return hipGetLastError();
 }

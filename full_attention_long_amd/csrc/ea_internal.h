@@ -224,13 +224,27 @@ struct BwdArgs {
   const Item* items;
   const int32_t* order;
   const int32_t* meta;
-  int64_t T, max_items;
-  int32_t B, Hq, Hkv, G, BMq, n_sink, stamp;
+  const int32_t* dkv_order;  // dK/dV items in cost order
+  int64_t T, max_items, dkv_n;
+  int32_t B, Hq, Hkv, G, BMq, n_sink, stamp, npair;
   float scale;
 };
 
-hipError_t launch_backward(const Shape& s, const Geometry& g, const BwdArgs& args,
-                           const int64_t dkv_items, hipStream_t st);
+// Keys per workgroup of the dK/dV kernel (16 per wave).
+constexpr int kDkvWaves = 8;
+constexpr int kDkvKeys = 16 * kDkvWaves;
+
+// Cost-ordered list of the dK/dV kernel's items (sequence, KV head, key
+// group), in its own workspace region.
+struct DkvList {
+  size_t keys_in, keys_out, vals_in, order, sort_tmp, sort_tmp_bytes, total;
+  int64_t n;
+  int32_t npair, maxcost;
+};
+DkvList dkv_list_layout(const Shape& s);
+
+hipError_t launch_backward(const Shape& s, const Geometry& g, BwdArgs args, const DkvList& l,
+                           char* list_base, hipStream_t st);
 
 // Training-forward helpers (ea_dual.hip).
 hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float tau, int64_t n,
