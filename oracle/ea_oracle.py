@@ -406,6 +406,33 @@ def _mix(O_fa, O_sa, cu_seqlens, r):
     return O
 
 
+def router_logit_grad(dO, O_fa, O_sa, cu_seqlens, r_soft, tau: float):
+    """Gradient of the loss with respect to the routing logits z through the
+    straight-through estimator, for the upstream gradient dO of the mixed
+    output O = r[0] O_FA + r[1] O_SA.
+
+    The STE passes the gradient of r straight to r_soft: dr[b, g, m] =
+    sum over the tokens of sequence b and the query heads of KV head g of
+    <dO, O_m>.  Through r_soft = softmax((z + g) / tau):
+    dz = r_soft * (dr - <dr, r_soft>) / tau.  Returns (dz, dr) float64
+    [B, Hkv, 2]."""
+    T, Hq, d = dO.shape
+    B = len(cu_seqlens) - 1
+    Hkv = r_soft.shape[1]
+    G = Hq // Hkv
+    dr = np.zeros((B, Hkv, 2), dtype=np.float64)
+    for b in range(B):
+        s0, e0 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        for hq in range(Hq):
+            g = hq // G
+            do = np.asarray(dO[s0:e0, hq], np.float64)
+            dr[b, g, 0] += float((do * np.asarray(O_fa[s0:e0, hq], np.float64)).sum())
+            dr[b, g, 1] += float((do * np.asarray(O_sa[s0:e0, hq], np.float64)).sum())
+    rs = np.asarray(r_soft, np.float64)
+    dz = rs * (dr - (dr * rs).sum(axis=-1, keepdims=True)) / float(np.float32(tau))
+    return dz, dr
+
+
 def dual_attention_rows(Q, K, V, cu_seqlens, r_soft, modes, tokens, heads, *, block=64, n_sink=1,
                         window_blocks=0, keep_fraction=0.2, softmax_scale=0.0):
     """dual_attention at selected global token indices and query heads only.

@@ -272,3 +272,38 @@ def test_backward_invariants():
         # dV sums dO over the queries weighted by probabilities that sum to 1 per row
         np.testing.assert_allclose(dV.sum(axis=0),
                                    dO.reshape(L, Hkv, Hq // Hkv, d).sum(axis=(0, 2)), atol=1e-10)
+
+
+def test_router_logit_grad_matches_autograd_through_the_ste():
+    # torch autograd through y = (z + g) / tau, r_soft = softmax(y),
+    # r = onehot(argmax) - r_soft.detach() + r_soft, O = r0 O_FA + r1 O_SA,
+    # loss = <dO, O>
+    lengths = [40, 0, 77]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    Hq, Hkv, d = 6, 2, 8
+    dO, O_fa, O_sa = _rand(130, T, Hq, d), _rand(131, T, Hq, d), _rand(132, T, Hq, d)
+    z, g = _rand(133, 3, Hkv, 2), _rand(134, 3, Hkv, 2)
+    tau = 0.7
+    r_soft, modes = orc.gumbel_route(z, g, tau)
+    dz, dr = orc.router_logit_grad(dO, O_fa, O_sa, cu, r_soft, tau)
+    zt = torch.tensor(z.astype(np.float32).astype(np.float64), requires_grad=True)
+    y = (zt + torch.tensor(g.astype(np.float32).astype(np.float64))) / float(np.float32(tau))
+    rs = torch.softmax(y, dim=-1)
+    hard = torch.nn.functional.one_hot(rs.argmax(-1), 2).double()
+    r = hard - rs.detach() + rs
+    loss = 0.0
+    G = Hq // Hkv
+    for b in range(3):
+        s0, e0 = cu[b], cu[b + 1]
+        for hq in range(Hq):
+            rb = r[b, hq // G]
+            o = rb[0] * torch.from_numpy(O_fa[s0:e0, hq]) + rb[1] * torch.from_numpy(O_sa[s0:e0, hq])
+            loss = loss + (o * torch.from_numpy(dO[s0:e0, hq])).sum()
+    loss.backward()
+    # the oracle rounds y = (z + g) / tau to float32 (the precision the hard
+    # decision is taken in); autograd runs in float64: 2^-24 relative apart
+    np.testing.assert_allclose(dz, zt.grad.numpy(), rtol=1e-6, atol=1e-9)
+    # dr itself: an empty sequence has none; dz sums to zero over the two modes
+    assert np.all(dr[1] == 0)
+    np.testing.assert_allclose(dz.sum(-1), 0.0, atol=1e-12)
