@@ -26,6 +26,8 @@ from .binding import (  # noqa: F401
     ea_last_error,
     ea_mfma_probe,
     ea_route,
+    ea_router_logit_grad,
+    ea_router_logit_grad_workspace_size,
     header_functions,
     lib,
 )

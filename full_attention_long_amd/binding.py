@@ -105,6 +105,11 @@ def lib() -> ctypes.CDLL:
     L.ea_hybrid_backward.restype = i32
     L.ea_hybrid_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32,
                                      i32, ctypes.POINTER(SparsityParams), vp, vp, vp, vp, sz, vp]
+    L.ea_router_logit_grad_workspace_size.restype = sz
+    L.ea_router_logit_grad_workspace_size.argtypes = [i32, i32, i32]
+    L.ea_router_logit_grad.restype = i32
+    L.ea_router_logit_grad.argtypes = [vp, vp, vp, i32, vp, i32, i64, i32, i32, i32, i32, vp,
+                                       ctypes.c_float, vp, vp, vp, sz, vp]
     L.ea_mfma_probe.restype = i32
     L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
@@ -277,6 +282,34 @@ def ea_hybrid_backward(Q, K, V, O, dO, lse, modes, cu_seqlens, max_seqlen: int, 
                                     ctypes.byref(sp), _ptr(dQ), _ptr(dK), _ptr(dV),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
     return dQ, dK, dV
+
+
+def ea_router_logit_grad_workspace_size(B: int, max_seqlen: int, Hkv: int) -> int:
+    return int(lib().ea_router_logit_grad_workspace_size(B, max_seqlen, Hkv))
+
+
+def ea_router_logit_grad(dO, O_fa, O_sa, cu_seqlens, max_seqlen: int, r_soft, tau: float, *,
+                         dz=None, dr=None, with_dr: bool = True, workspace=None, stream=None):
+    """(dz, dr) float32 [B, Hkv, 2]: the routing logits' gradient through the
+    straight-through estimator and the Gumbel-Softmax."""
+    import torch
+    for t, n in [(dO, "dO"), (O_fa, "O_fa"), (O_sa, "O_sa"), (cu_seqlens, "cu_seqlens"),
+                 (r_soft, "r_soft")]:
+        _dev(t, n)
+    T, Hq, d = dO.shape
+    B = cu_seqlens.numel() - 1
+    Hkv = r_soft.shape[1]
+    dz = torch.empty_like(r_soft) if dz is None else dz
+    if dr is None and with_dr:
+        dr = torch.empty_like(r_soft)
+    if workspace is None:
+        workspace = torch.empty(max(1, ea_router_logit_grad_workspace_size(B, max_seqlen, Hkv)),
+                                dtype=torch.uint8, device=dO.device)
+    _check(lib().ea_router_logit_grad(_ptr(dO), _ptr(O_fa), _ptr(O_sa), _dtype_code(dO),
+                                      _ptr(cu_seqlens), B, T, max_seqlen, Hq, Hkv, d,
+                                      _ptr(r_soft), float(tau), _ptr(dz), _ptr(dr),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dz, dr
 
 
 def ea_gumbel_route(logits, tau: float, *, gumbel=None, r_soft=None, modes=None,

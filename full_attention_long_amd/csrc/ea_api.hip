@@ -476,6 +476,33 @@ ea_status ea_hybrid_backward(const void* Q, const void* K, const void* V, const 
   return ok();
 }
 
+size_t ea_router_logit_grad_workspace_size(int32_t B, int32_t max_seqlen, int32_t Hkv) {
+  if (B < 1 || Hkv < 1 || max_seqlen < 1) return 0;
+  g_err.clear();
+  return static_cast<size_t>(B) * Hkv * ea::logit_grad_chunks(max_seqlen) * 2 * sizeof(float);
+}
+
+ea_status ea_router_logit_grad(const void* dO, const void* O_fa, const void* O_sa, ea_dtype dtype,
+                               const int32_t* cu_seqlens, int32_t B, int64_t total_tokens,
+                               int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                               const float* r_soft, float tau, float* dz, float* dr,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea_status st = check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s);
+  if (st != EA_OK) return st;
+  if (!dO || !O_fa || !O_sa || !cu_seqlens || !r_soft || !dz)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!(tau > 0.f) || isinf(tau)) return fail(EA_ERR_INVALID_ARG, "tau must be finite and > 0");
+  const size_t need = ea_router_logit_grad_workspace_size(B, s.max_seqlen, Hkv);
+  if (!workspace || workspace_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = ea::launch_logit_grad(s, cu_seqlens, dO, O_fa, O_sa, r_soft, tau, dz, dr,
+                                       static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "logit gradient launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ea_status ea_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,
                         int64_t* flops, void* stream) {
   if (!out) return fail(EA_ERR_INVALID_ARG, "null pointer argument");

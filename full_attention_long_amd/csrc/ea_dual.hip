@@ -104,7 +104,93 @@ __global__ __launch_bounds__(256) void dual_merge_kernel(
   }
 }
 
+// Router-logit gradient, stage 1: per (sequence, KV head, chunk of
+// kGradChunk tokens) the sums over its tokens and the G query heads of
+// <dO, O_FA> and <dO, O_SA>; a workgroup reduces in a fixed order.
+constexpr int kGradChunk = 256;
+
+template <typename E>
+__global__ __launch_bounds__(256) void logit_grad_partial_kernel(
+    const int32_t* __restrict__ cu, int32_t B, int32_t Hkv, int32_t G, int32_t Hq, int32_t d,
+    int32_t nchunk, const E* __restrict__ dO, const E* __restrict__ O_fa,
+    const E* __restrict__ O_sa, float* __restrict__ part) {
+  __shared__ float red[2][4];
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int t0 = cu[b] + chunk * kGradChunk, t1 = min(cu[b + 1], t0 + kGradChunk);
+  const int row_elems = G * d;  // the group's heads are contiguous in a token row
+  float a0 = 0.f, a1 = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    const int64_t base = (static_cast<int64_t>(t) * Hq + static_cast<int64_t>(g) * G) * d;
+    for (int e = tid; e < row_elems; e += 256) {
+      const float x = static_cast<float>(dO[base + e]);
+      a0 += x * static_cast<float>(O_fa[base + e]);
+      a1 += x * static_cast<float>(O_sa[base + e]);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    a0 += __shfl_xor(a0, off, 64);
+    a1 += __shfl_xor(a1, off, 64);
+  }
+  if (tid % 64 == 0) {
+    red[0][tid / 64] = a0;
+    red[1][tid / 64] = a1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t pi = ((static_cast<int64_t>(b) * Hkv + g) * nchunk + chunk) * 2;
+    part[pi] = t0 < t1 ? (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]) : 0.f;
+    part[pi + 1] = t0 < t1 ? (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]) : 0.f;
+  }
+}
+
+// Stage 2: dr = the chunks' sums in order, then through the Gumbel-Softmax:
+// dz = r_soft * (dr - <dr, r_soft>) / tau.
+__global__ __launch_bounds__(256) void logit_grad_final_kernel(const float* __restrict__ part,
+                                                               int64_t n, int32_t nchunk,
+                                                               const float* __restrict__ r_soft,
+                                                               float tau, float* __restrict__ dz,
+                                                               float* __restrict__ dr) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float d0 = 0.f, d1 = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    d0 += part[(i * nchunk + c) * 2];
+    d1 += part[(i * nchunk + c) * 2 + 1];
+  }
+  const float r0 = r_soft[2 * i], r1 = r_soft[2 * i + 1];
+  const float mean = d0 * r0 + d1 * r1;
+  dz[2 * i] = r0 * (d0 - mean) / tau;
+  dz[2 * i + 1] = r1 * (d1 - mean) / tau;
+  if (dr) {
+    dr[2 * i] = d0;
+    dr[2 * i + 1] = d1;
+  }
+}
+
 }  // namespace
+
+int32_t logit_grad_chunks(int32_t max_seqlen) { return (max_seqlen + kGradChunk - 1) / kGradChunk; }
+
+hipError_t launch_logit_grad(const Shape& s, const int32_t* cu, const void* dO, const void* O_fa,
+                             const void* O_sa, const float* r_soft, float tau, float* dz, float* dr,
+                             float* part, hipStream_t st) {
+  const int32_t nchunk = logit_grad_chunks(s.max_seqlen);
+  const dim3 grid(static_cast<unsigned>(nchunk), static_cast<unsigned>(s.Hkv), static_cast<unsigned>(s.B));
+  if (s.elem_bytes == 2)
+    hipLaunchKernelGGL((logit_grad_partial_kernel<__bf16>), grid, dim3(256), 0, st, cu, s.B, s.Hkv,
+                       s.G, s.Hq, s.d, nchunk, static_cast<const __bf16*>(dO),
+                       static_cast<const __bf16*>(O_fa), static_cast<const __bf16*>(O_sa), part);
+  else
+    hipLaunchKernelGGL((logit_grad_partial_kernel<float>), grid, dim3(256), 0, st, cu, s.B, s.Hkv,
+                       s.G, s.Hq, s.d, nchunk, static_cast<const float*>(dO),
+                       static_cast<const float*>(O_fa), static_cast<const float*>(O_sa), part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(s.B) * s.Hkv;
+  hipLaunchKernelGGL(logit_grad_final_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, st, part, n, nchunk, r_soft, tau, dz, dr);
+  return hipGetLastError();
+}
 
 hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float tau, int64_t n,
                                float* r_soft, int8_t* modes, hipStream_t st) {

@@ -246,6 +246,13 @@ DkvList dkv_list_layout(const Shape& s);
 hipError_t launch_backward(const Shape& s, const Geometry& g, BwdArgs args, const DkvList& l,
                            char* list_base, hipStream_t st);
 
+// Router-logit gradient through the straight-through estimator (ea_dual.hip):
+// chunks of tokens per sequence for the partial sums, and the launcher.
+int32_t logit_grad_chunks(int32_t max_seqlen);
+hipError_t launch_logit_grad(const Shape& s, const int32_t* cu, const void* dO, const void* O_fa,
+                             const void* O_sa, const float* r_soft, float tau, float* dz, float* dr,
+                             float* part, hipStream_t st);
+
 // Training-forward helpers (ea_dual.hip).
 hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float tau, int64_t n,
                                float* r_soft, int8_t* modes, hipStream_t st);

@@ -240,6 +240,25 @@ ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype 
                           void* O_fa, void* O_sa, float* lse_fa, float* lse_sa, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ea_router_logit_grad - gradient of the loss with respect to the routing
+ * logits through the straight-through estimator and the Gumbel-Softmax
+ * (paper body: STE paragraph; summary Sec. 2.2).  With O = r[0] O_fa +
+ * r[1] O_sa per (sequence b, KV head g) and r = r_hard - sg(r_soft) + r_soft:
+ *   dr[b, g, m] = sum over b's tokens and g's query heads of <dO, O_m>,
+ *   dz = r_soft * (dr - <dr, r_soft>) / tau.
+ *
+ *   dO, O_fa, O_sa  [T, Hq, head_dim] of `dtype` (O_fa, O_sa from ea_dual_prefill)
+ *   r_soft          float32 [B, Hkv, 2] (from ea_gumbel_route), tau as there
+ *   dz              out float32 [B, Hkv, 2]; dr out float32 [B, Hkv, 2] or NULL
+ *   workspace       >= ea_router_logit_grad_workspace_size() bytes
+ * Sums run in a fixed order (no atomics): bitwise reproducible. */
+size_t ea_router_logit_grad_workspace_size(int32_t B, int32_t max_seqlen, int32_t Hkv);
+ea_status ea_router_logit_grad(const void* dO, const void* O_fa, const void* O_sa, ea_dtype dtype,
+                               const int32_t* cu_seqlens, int32_t B, int64_t total_tokens,
+                               int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                               const float* r_soft, float tau, float* dz, float* dr,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace ea_hybrid_backward needs (0 if the sizes are
  * invalid): the forward's work list plus two float32 [Hq, T] arrays. */
 size_t ea_hybrid_backward_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,

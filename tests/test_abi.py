@@ -20,7 +20,8 @@ def test_every_header_function_is_exported():
                           "ea_gumbel_route", "ea_dual_prefill_workspace_size", "ea_dual_prefill",
                           "ea_kvcache_bytes", "ea_kvcache_init", "ea_kvcache_prefill",
                           "ea_decode_workspace_size", "ea_decode_step",
-                          "ea_hybrid_backward_workspace_size", "ea_hybrid_backward"}
+                          "ea_hybrid_backward_workspace_size", "ea_hybrid_backward",
+                          "ea_router_logit_grad_workspace_size", "ea_router_logit_grad"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n

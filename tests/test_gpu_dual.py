@@ -139,3 +139,31 @@ def test_dual_full_size_sampled():
     assert np.abs(lse_sa[heads][:, tt].T.cpu().numpy() - ref[4]).max() <= LSE_TOL
     for t in (O, O_fa, O_sa, lse_fa, lse_sa):
         assert bool(torch.isfinite(t).all())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_router_logit_grad_matches_oracle(dtype):
+    lengths = [700, 0, 1, 333]
+    c = gen.custom_case(61, lengths, 8, 2, 64, dtype, n_sink=1, keep_fraction=0.25)
+    z, g = _route_inputs(17, len(lengths), 2)
+    tau = 0.6
+    zt, gt = torch.from_numpy(z).cuda(), torch.from_numpy(g).cuda()
+    r_soft, modes = ea.ea_gumbel_route(zt, tau, gumbel=gt)
+    note(f"router logit grad {dtype}")
+    O, O_fa, O_sa, _, _ = _gpu_dual(c, modes.cpu().numpy())
+    dOn = gen.normal(5, 40, (c.T, 8, 64))
+    dO = dev_tensor(gen.bf16_bits(dOn) if dtype == "bf16" else dOn, dtype)
+    dz, dr = ea.ea_router_logit_grad(dO, O_fa, O_sa, torch.from_numpy(c.cu_seqlens).cuda(),
+                                     int(max(lengths)), r_soft, tau)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    ref_dz, ref_dr = orc.router_logit_grad(f(dO), f(O_fa), f(O_sa), c.cu_seqlens,
+                                           r_soft.cpu().numpy(), tau)
+    s = max(float(np.abs(ref_dr).max()), 1e-30)
+    assert np.abs(dr.cpu().numpy() - ref_dr).max() <= 1e-5 * s
+    assert np.abs(dz.cpu().numpy() - ref_dz).max() <= 1e-5 * max(float(np.abs(ref_dz).max()), 1e-30) + 1e-6
+    assert np.all(dr.cpu().numpy()[1] == 0)            # the empty sequence
+    # reproducible bit for bit
+    dz2, _ = ea.ea_router_logit_grad(dO, O_fa, O_sa, torch.from_numpy(c.cu_seqlens).cuda(),
+                                     int(max(lengths)), r_soft, tau)
+    assert torch.equal(dz, dz2)
