@@ -34,8 +34,6 @@
 // a row's probabilities sum past 2^20.  Either way the ratio O / l is exact.
 #include "ea_internal.h"
 
-#include <type_traits>
-
 namespace ea {
 namespace {
 
@@ -97,22 +95,17 @@ __device__ __forceinline__ i16x4 ds_read_tr(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
-  f32x8 v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = s[base + e];
-  return __builtin_convertvector(v, bf16x8);
-}
-
-template <bool BF16, int D>
-__global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs a) {
-  using E = std::conditional_t<BF16, uint16_t, float>;
+// ---------------------------------------------------------------------------
+// float32 kernel (the correctness path): 32x32x2 fp32 MFMAs, K and V tiles
+// staged through registers into padded LDS rows, double-buffered.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_f32(AttnArgs a) {
+  using E = float;
   constexpr int NT = kAttnWaves * 64;      // threads per workgroup
   constexpr int CH = 16 / sizeof(E);       // elements per 16-byte chunk
   constexpr int KROW = D + CH;             // padded LDS row of K (elements)
-  // padded LDS row of V: 64 bytes of pad put the 4 rows one transposing read
-  // touches on disjoint bank ranges (bf16); the fp32 path reads single words
-  constexpr int VROW = BF16 ? D + 32 : D + CH;
+  constexpr int VROW = D + CH;             // padded LDS row of V (elements)
   constexpr int NLD = kBlock * D / CH / NT;  // 16-byte chunks per thread per block (K and V each)
   constexpr int DT = D / 32;               // 32-wide dim tiles of O^T
   static_assert(NLD * NT * CH == kBlock * D, "tile must split evenly over the workgroup");
@@ -156,15 +149,15 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
   const E* Vp = static_cast<const E*>(a.V);
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
-  using QFrag = std::conditional_t<BF16, bf16x8, f32x4>;
-  constexpr int NQ = BF16 ? D / 16 : D / 8;
+  using QFrag = f32x4;
+  constexpr int NQ = D / 8;
   QFrag qf[NQ];
   {
     const E* qrow = Qp + (static_cast<int64_t>(tok0 + pos) * a.Hq + hq) * D;
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       if (rvalid) {
-        qf[u] = *reinterpret_cast<const QFrag*>(qrow + (BF16 ? 16 * u : 8 * u) + 4 * (BF16 ? 2 : 1) * h);
+        qf[u] = *reinterpret_cast<const QFrag*>(qrow + 8 * u + 4 * h);
       } else {
         qf[u] = QFrag{};
       }
@@ -219,24 +212,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     const E* k0 = &Ks[buf][lq * KROW];
     const E* k1 = &Ks[buf][(32 + lq) * KROW];
-    if constexpr (BF16) {
 #pragma unroll
-      for (int u = 0; u < D / 16; ++u) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k0 + 16 * u + 8 * h);
-        const bf16x8 kb2 = *reinterpret_cast<const bf16x8*>(k1 + 16 * u + 8 * h);
-        s0 = mfma_bf16(ka, qf[u], s0);
-        s1 = mfma_bf16(kb2, qf[u], s1);
-      }
-    } else {
+    for (int g = 0; g < D / 8; ++g) {
+      const f32x4 ka = *reinterpret_cast<const f32x4*>(k0 + 8 * g + 4 * h);
+      const f32x4 kb2 = *reinterpret_cast<const f32x4*>(k1 + 8 * g + 4 * h);
 #pragma unroll
-      for (int g = 0; g < D / 8; ++g) {
-        const f32x4 ka = *reinterpret_cast<const f32x4*>(k0 + 8 * g + 4 * h);
-        const f32x4 kb2 = *reinterpret_cast<const f32x4*>(k1 + 8 * g + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s0 = mfma_f32(ka[e], qf[g][e], s0);
-          s1 = mfma_f32(kb2[e], qf[g][e], s1);
-        }
+      for (int e = 0; e < 4; ++e) {
+        s0 = mfma_f32(ka[e], qf[g][e], s0);
+        s1 = mfma_f32(kb2[e], qf[g][e], s1);
       }
     }
 
@@ -279,36 +262,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
     l_run += ls;
 
     // ---- O^T += V^T P^T ----
-    if constexpr (BF16) {
-      bf16x8 pb[4];
-      pb[0] = to_bf16x8(s0, 0);
-      pb[1] = to_bf16x8(s0, 8);
-      pb[2] = to_bf16x8(s1, 0);
-      pb[3] = to_bf16x8(s1, 8);
-      // lane (group g16 of 16 lanes, i16 within it) reads rows 4h + i16/4 (+16u, +8 for
-      // the upper 4 keys) at columns 16 (g16 & 1) + 4 (i16 & 3) (+32t): the result is
-      // V[16u + 4h + 0..3 (+8)][32t + lq], the A operand for keys in P^T's order
-      const E* vb = &Vs[buf][(4 * h + (lane & 15) / 4) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
+    for (int t = 0; t < DT; ++t) {
+      const E* vcol = &Vs[buf][32 * t + lq];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const i16x4 lo = ds_read_tr(vb + 16 * u * VROW + 32 * t);
-          const i16x4 hi = ds_read_tr(vb + (16 * u + 8) * VROW + 32 * t);
-          const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, v8), pb[u], o[t]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const E* vcol = &Vs[buf][32 * t + lq];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 8 * (i / 4) + 4 * h + (i % 4);
-          o[t] = mfma_f32(vcol[key * VROW], s0[i], o[t]);
-          o[t] = mfma_f32(vcol[(key + 32) * VROW], s1[i], o[t]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i / 4) + 4 * h + (i % 4);
+        o[t] = mfma_f32(vcol[key * VROW], s0[i], o[t]);
+        o[t] = mfma_f32(vcol[(key + 32) * VROW], s1[i], o[t]);
       }
     }
 
@@ -327,18 +288,10 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel(AttnArgs 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int dim = 32 * t + 8 * q + 4 * h;
-        if constexpr (BF16) {
-          f32x4 v;
+        f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = o[t][4 * q + e] * inv;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          *reinterpret_cast<bf16x4*>(orow + dim) = __builtin_convertvector(v, bf16x4);
-        } else {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = o[t][4 * q + e] * inv;
-          *reinterpret_cast<f32x4*>(orow + dim) = v;
-        }
+        for (int e = 0; e < 4; ++e) v[e] = o[t][4 * q + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + dim) = v;
       }
     }
     if (h == 0 && lse_out)
@@ -644,7 +597,7 @@ void launch(const AttnArgs& args, unsigned grid, hipStream_t st) {
   if constexpr (BF16)
     hipLaunchKernelGGL((attention_kernel_bf16<D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
   else
-    hipLaunchKernelGGL((attention_kernel<false, D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+    hipLaunchKernelGGL((attention_kernel_f32<D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
 }
 
 }  // namespace
