@@ -556,9 +556,13 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     if (!full) mask(kb, c0, c1);
     dma(Kseq, dma_koff, kload, KGS, kb_of(min(n + 2, nblk - 1)));
     dma(Vseq, dma_voff, vload, RPI * D, kb_of(min(n + 1, nblk - 1)));
+    // a wave in the score / softmax phase issues ahead of one in the O += V P
+    // phase on the same SIMD (its VALU work is what the other's MFMAs hide)
+    __builtin_amdgcn_s_setprio(1);
     scores(kread, x0, x1);
     bf16x8 pb[4];
     softmax(c0, c1, pb);
+    __builtin_amdgcn_s_setprio(0);
     pv(vread, pb);
     __syncthreads();
   };
