@@ -6,8 +6,10 @@ throughput.
 """
 from .binding import (  # noqa: F401
     EAError,
+    HEAD_CONFIGS,
     KVCache,
     KVCacheDesc,
+    XAParams,
     ea_decode_step,
     ea_decode_workspace_size,
     ea_kvcache_bytes,
@@ -28,6 +30,8 @@ from .binding import (  # noqa: F401
     ea_route,
     ea_router_logit_grad,
     ea_router_logit_grad_workspace_size,
+    ea_xa_prefill,
+    ea_xa_prefill_workspace_size,
     header_functions,
     lib,
 )

@@ -43,6 +43,17 @@ class SparsityParams(ctypes.Structure):
     ]
 
 
+class XAParams(ctypes.Structure):
+    _fields_ = [
+        ("block", ctypes.c_int32), ("stride", ctypes.c_int32),
+        ("threshold", ctypes.c_float), ("head_config", ctypes.c_int32),
+    ]
+
+
+EA_HEADS_FA_SSA, EA_HEADS_FA_XA, EA_HEADS_XA_SSA = 0, 1, 2
+HEAD_CONFIGS = {"FA-SSA": EA_HEADS_FA_SSA, "FA-XA": EA_HEADS_FA_XA, "XA-SSA": EA_HEADS_XA_SSA}
+
+
 class KVCacheDesc(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -110,6 +121,12 @@ def lib() -> ctypes.CDLL:
     L.ea_router_logit_grad.restype = i32
     L.ea_router_logit_grad.argtypes = [vp, vp, vp, i32, vp, i32, i64, i32, i32, i32, i32, vp,
                                        ctypes.c_float, vp, vp, vp, sz, vp]
+    L.ea_xa_prefill_workspace_size.restype = sz
+    L.ea_xa_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.ea_xa_prefill.restype = i32
+    L.ea_xa_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                ctypes.POINTER(SparsityParams), ctypes.POINTER(XAParams), vp, vp,
+                                vp, vp, vp, sz, vp]
     L.ea_mfma_probe.restype = i32
     L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
@@ -248,6 +265,45 @@ def ea_hybrid_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace
                                        _ptr(cu_seqlens), B, T, max_seqlen, Hq, Hkv, d,
                                        ctypes.byref(sp), _ptr(out), _ptr(lse), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def ea_xa_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype_code):
+    return int(lib().ea_xa_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_dim,
+                                                  dtype_code))
+
+
+def ea_xa_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, head_config="XA-SSA",
+                  threshold: float = 0.9, xa_block: int = 128, stride: int = 8, n_sink: int = 1,
+                  window_blocks: int = 0, keep_fraction: float = 0.2, softmax_scale: float = 0.0,
+                  block: int = 64, out=None, lse=None, with_lse: bool = True, mass=None,
+                  keep=None, workspace=None, stream=None):
+    """O [T, Hq, d] (and LSE float32 [Hq, T]) of the hybrid prefill with XA heads.
+
+    ``head_config`` is "FA-SSA", "FA-XA" or "XA-SSA" (or its ea_head_config
+    code).  ``mass`` / ``keep`` (float32 / uint8 [B, Hq, nqb, nqb] device
+    tensors, nqb = ceil(max_seqlen / xa_block)) receive the XA heads' block
+    masses and keep flags when given."""
+    import torch
+    cfg = HEAD_CONFIGS[head_config] if isinstance(head_config, str) else int(head_config)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    B = cu_seqlens.numel() - 1
+    code = _dtype_code(Q)
+    if workspace is None:
+        need = ea_xa_prefill_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    T, Hq, Hkv, d, B, code, out, lse, workspace = _prefill_args(
+        Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen)
+    for t, n in [(mass, "mass"), (keep, "keep")]:
+        if t is not None:
+            _dev(t, n)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    xp = XAParams(xa_block, stride, threshold, cfg)
+    _check(lib().ea_xa_prefill(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes), _ptr(cu_seqlens), B, T,
+                               max_seqlen, Hq, Hkv, d, ctypes.byref(sp), ctypes.byref(xp), _ptr(out),
+                               _ptr(lse), _ptr(mass), _ptr(keep), _ptr(workspace),
+                               workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libea.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["ea_api.hip", "ea_route.hip", "ea_worklist.hip", "ea_attention.hip", "ea_dual.hip", "ea_decode.hip", "ea_backward.hip", "ea_probe.hip"]
+SOURCES = ["ea_api.hip", "ea_route.hip", "ea_worklist.hip", "ea_attention.hip", "ea_dual.hip", "ea_decode.hip", "ea_backward.hip", "ea_probe.hip", "ea_xa.hip"]
 # The attention kernels never rely on NaN semantics (masked scores are set to
 # -inf by selects on integer conditions); without NaN handling a row max is
 # one v_max3 per two scores instead of a canonicalize + max per score.

@@ -76,8 +76,10 @@ struct AttnArgs {
   const Item* items;
   const int32_t* order;
   const int32_t* meta;
+  const int32_t* xa_list;  // XA mode: kept key blocks per (sequence, KV head, XA query block)
+  const int32_t* xa_cnt;
   int64_t T;
-  int32_t Hq, Hkv, G, BMq, n_sink, stamp, parts;
+  int32_t Hq, Hkv, G, BMq, n_sink, stamp, parts, xa_nqb;
   float scale_log2;
 };
 
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_f32(AttnA
 // sequence end, so rows past it read as zeros.  LDS operand reads run a few
 // MFMAs ahead of their use.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool XA>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(AttnArgs a) {
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
   constexpr int TILE = kBlock * D;               // elements of one K or V tile
@@ -357,8 +359,25 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   const int qb0 = p0 / kBlock, qb1 = p1 / kBlock;
   const KeyRange kr = key_range(mode, qb0, qb1, ns, w);
   const int r1_end = kr.r1_end, r2_beg = kr.r2_beg;
-  const int nblk = kr.count();
-  auto kb_of = [&](int n) { return n < r1_end ? n : r2_beg + (n - r1_end); };
+  int nblk = kr.count();
+  // XA item: the ascending list of the tile's XA query block (entries
+  // j | head mask << 16 for kept 128-blocks j, each two 64-blocks), less the
+  // diagonal block's second half when the tile ends before it
+  const int32_t* xl = nullptr;
+  if constexpr (XA) {
+    if (mode == kModeXA) {
+      const int xi = p0 / kXaBlock;
+      const int64_t bk = static_cast<int64_t>(b) * a.Hkv + kvh;
+      xl = a.xa_list + bk * xa_row_offset(a.xa_nqb) + xa_row_offset(xi);
+      nblk = 2 * a.xa_cnt[bk * a.xa_nqb + xi] - (2 * xi + 1 > qb1 ? 1 : 0);
+    }
+  }
+  auto kb_of = [&](int n) {
+    if constexpr (XA) {
+      if (mode == kModeXA) return 2 * (xl[n >> 1] & 0xFFFF) + (n & 1);
+    }
+    return n < r1_end ? n : r2_beg + (n - r1_end);
+  };
   uint16_t* const Oout = static_cast<uint16_t*>(mode == kModeMiddle ? a.O_mid : a.O);
   float* const lse_out = mode == kModeMiddle ? a.lse_mid : a.lse;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -465,8 +484,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     }
   };
 
-  auto mask = [&](int kb, f32x16& s0, f32x16& s1) {
-    const bool blk_ok = block_visible(mode, kb, qblk, ns, w);
+  // hmask: XA heads of the group that kept block kb (XA items only)
+  auto mask = [&](int kb, uint32_t hmask, f32x16& s0, f32x16& s1) {
+    bool blk_ok;
+    if constexpr (XA) {
+      blk_ok = mode == kModeXA ? ((hmask >> hh) & 1u) != 0u : block_visible(mode, kb, qblk, ns, w);
+    } else {
+      blk_ok = block_visible(mode, kb, qblk, ns, w);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
@@ -552,8 +577,19 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   auto iter = [&](int n, f32x16& c0, f32x16& c1, f32x16& x0, f32x16& x1, uint16_t* kload,
                   const uint16_t* kread, uint16_t* vload, const uint16_t* vread) {
     const int kb = kb_of(n);
-    const bool full = block_full(mode, kb, p0, qb0, qb1, ns, w);
-    if (!full) mask(kb, c0, c1);
+    uint32_t hmask = 0u;
+    bool full;
+    if constexpr (XA) {
+      if (mode == kModeXA) {
+        hmask = static_cast<uint32_t>(xl[n >> 1]) >> 16;
+        full = hmask == (1u << a.G) - 1u && kb * kBlock + kBlock - 1 <= p0;
+      } else {
+        full = block_full(mode, kb, p0, qb0, qb1, ns, w);
+      }
+    } else {
+      full = block_full(mode, kb, p0, qb0, qb1, ns, w);
+    }
+    if (!full) mask(kb, hmask, c0, c1);
     dma(Kseq, dma_koff, kload, KGS, kb_of(min(n + 2, nblk - 1)));
     dma(Vseq, dma_voff, vload, RPI * D, kb_of(min(n + 1, nblk - 1)));
     // a wave in the score / softmax phase issues ahead of one in the O += V P
@@ -597,11 +633,15 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
 }
 
 template <bool BF16, int D>
-void launch(const AttnArgs& args, unsigned grid, hipStream_t st) {
-  if constexpr (BF16)
-    hipLaunchKernelGGL((attention_kernel_bf16<D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-  else
+void launch(const AttnArgs& args, unsigned grid, bool xa, hipStream_t st) {
+  if constexpr (BF16) {
+    if (xa)
+      hipLaunchKernelGGL((attention_kernel_bf16<D, true>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+    else
+      hipLaunchKernelGGL((attention_kernel_bf16<D, false>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+  } else {
     hipLaunchKernelGGL((attention_kernel_f32<D>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
+  }
 }
 
 }  // namespace
@@ -631,13 +671,19 @@ hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, co
   a.stamp = plan_stamp(s);
   a.parts = s.parts;
   a.scale_log2 = g.scale_log2;
+  a.xa_list = s.xa ? reinterpret_cast<const int32_t*>(base + ws.xa_list) : nullptr;
+  a.xa_cnt = s.xa ? reinterpret_cast<const int32_t*>(base + ws.xa_cnt) : nullptr;
+  a.xa_nqb = ws.xa_nqb;
   constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
   const unsigned grid = static_cast<unsigned>((ws.max_items + span - 1) / span * span);
   const bool bf16 = s.elem_bytes == 2;
-  if (bf16 && s.d == 128) launch<true, 128>(a, grid, st);
-  else if (bf16 && s.d == 64) launch<true, 64>(a, grid, st);
-  else if (!bf16 && s.d == 128) launch<false, 128>(a, grid, st);
-  else launch<false, 64>(a, grid, st);
+  // XA items exist only in bf16 (the caller rejects float32 with XA heads)
+  const bool xa = s.xa != 0;
+  if (xa && !bf16) return hipErrorInvalidValue;
+  if (bf16 && s.d == 128) launch<true, 128>(a, grid, xa, st);
+  else if (bf16 && s.d == 64) launch<true, 64>(a, grid, xa, st);
+  else if (!bf16 && s.d == 128) launch<false, 128>(a, grid, xa, st);
+  else launch<false, 64>(a, grid, xa, st);
   return hipGetLastError();
 }
 

@@ -29,8 +29,28 @@ constexpr int kBlock = 64;
 enum ItemMode : int32_t {
   kModeFA = 0,      // every causal key block
   kModeSA = 1,      // sink blocks and the local window
-  kModeMiddle = 2   // the causal blocks SA leaves out: FA = SA set + middle set
+  kModeMiddle = 2,  // the causal blocks SA leaves out: FA = SA set + middle set
+  kModeXA = 3       // the key blocks the XAttention selection kept (ea_xa.hip)
 };
+
+// XAttention (XA) mode: blocks of kXaBlock tokens are selected by the
+// antidiagonal scores of position groups of kXaStride; one 128-token XA block
+// spans two 64-token attention blocks.
+constexpr int kXaBlock = 128;
+constexpr int kXaStride = 8;
+constexpr int kXaGroupsPerBlock = kXaBlock / kXaStride;
+
+// Computation mode of router decision r (0 retrieval head, 1 sparse head)
+// under an ea_head_config.
+__host__ __device__ inline int computation_mode(int head_config, int r) {
+  if (head_config == EA_HEADS_FA_XA) return r ? kModeXA : kModeFA;
+  if (head_config == EA_HEADS_XA_SSA) return r ? kModeSA : kModeXA;
+  return r ? kModeSA : kModeFA;
+}
+
+// Offset of query block i's list in the triangular per-(sequence, KV head)
+// array of kept key blocks: row i holds at most i + 1 entries.
+__host__ __device__ inline int64_t xa_row_offset(int64_t i) { return i * (i + 1) / 2; }
 
 // One attention work item: a query tile of one KV-head group of one sequence,
 // over one key-block set.
@@ -103,6 +123,11 @@ struct Workspace {
   size_t sort_tmp_bytes, total;
   int64_t max_items;   // bound on work items
   int32_t nbins;       // cost bins of the sort key
+  // XA mode only (Shape.xa): per (sequence, KV head, query block) the number
+  // of kept key blocks, and the triangular array of their list entries
+  // (key block j | per-head mask << 16, ascending j)
+  size_t xa_cnt, xa_list;
+  int32_t xa_nqb;      // query blocks of kXaBlock per sequence (upper bound)
 };
 
 struct Shape {
@@ -113,6 +138,10 @@ struct Shape {
   // work items per query tile: 1 for the routed forward (the head's own mode),
   // 2 for the dual-mode forward (SA set and middle set of every head)
   int32_t parts = 1;
+  // ea_head_config mapping router decisions to computation modes, and
+  // whether the workspace holds the XA selection lists
+  int32_t head_config = EA_HEADS_FA_SSA;
+  int32_t xa = 0;
 };
 
 Workspace plan_workspace(const Shape& s);
@@ -123,7 +152,7 @@ Workspace plan_workspace(const Shape& s);
 // unplanned (or differently planned) workspace never reads a stale list.
 inline int32_t plan_stamp(const Shape& s) {
   uint64_t h = 0x9E3779B97F4A7C15ull;
-  const int64_t v[7] = {s.B, s.T, s.Hq, s.Hkv, s.BMq, s.max_seqlen, s.parts};
+  const int64_t v[9] = {s.B, s.T, s.Hq, s.Hkv, s.BMq, s.max_seqlen, s.parts, s.head_config, s.xa};
   for (int64_t x : v) {
     h ^= static_cast<uint64_t>(x) + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
     h *= 0xBF58476D1CE4E5B9ull;
@@ -159,6 +188,16 @@ struct AttnOut {
 hipError_t launch_attention(const Shape& s, const Geometry& g, const void* Q, const void* K,
                             const void* V, const int32_t* cu, const AttnOut& out,
                             const Workspace& ws, char* base, hipStream_t st);
+
+// XAttention selection (ea_xa.hip): dynamic LDS bytes of its kernel (0 if the
+// sizes are not supported), and the launcher, which fills the workspace's
+// XA counts and lists for every XA head (optionally also the block masses and
+// keep flags, [B, Hq, nqb, nqb]).
+size_t xa_plan_lds_bytes(const Shape& s);
+hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const void* Q,
+                          const void* K, const int8_t* modes, const int32_t* cu,
+                          const Workspace& ws, char* base, float* mass, uint8_t* keep,
+                          hipStream_t st);
 
 // Mode-aware KV cache (ea_decode.hip): the device view of a cache buffer.
 struct CacheView {

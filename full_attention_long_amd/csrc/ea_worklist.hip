@@ -115,9 +115,10 @@ __host__ __device__ __forceinline__ uint32_t max_key(int32_t nbins) {
 // part 0 covers every head's SA set and part 1 the rest of its causal blocks.
 __global__ __launch_bounds__(256) void items_kernel(
     const int32_t* __restrict__ cu, const int8_t* __restrict__ modes, int32_t B, int32_t Hkv,
-    int32_t BMq, int32_t parts, int32_t n_sink, const int32_t* __restrict__ meta,
-    const int32_t* __restrict__ tile_prefix, const int32_t* __restrict__ seq_w, int32_t nbins,
-    int64_t max_items, Item* __restrict__ raw, uint32_t* __restrict__ keys,
+    int32_t BMq, int32_t parts, int32_t head_config, int32_t n_sink,
+    const int32_t* __restrict__ meta, const int32_t* __restrict__ tile_prefix,
+    const int32_t* __restrict__ seq_w, const int32_t* __restrict__ xa_cnt, int32_t xa_nqb,
+    int32_t nbins, int64_t max_items, Item* __restrict__ raw, uint32_t* __restrict__ keys,
     int32_t* __restrict__ vals) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (x >= max_items) return;
@@ -137,9 +138,18 @@ __global__ __launch_bounds__(256) void items_kernel(
   const int L = cu[b + 1] - cu[b];
   const int p0 = qt * BMq, p1 = min(p0 + BMq, L) - 1;
   int mode;
-  if (parts == 1) mode = modes[static_cast<int64_t>(b) * Hkv + kvh] != 0 ? kModeSA : kModeFA;
+  if (parts == 1) mode = computation_mode(head_config, modes[static_cast<int64_t>(b) * Hkv + kvh] != 0);
   else mode = part == 0 ? kModeSA : kModeMiddle;
-  const int cost = key_range(mode, p0 / kBlock, p1 / kBlock, n_sink, seq_w[b]).count();
+  int cost;
+  if (mode == kModeXA) {
+    // the kept 128-blocks of the tile's XA query block, two 64-blocks each,
+    // less the diagonal block's second half when the tile ends before it
+    const int i = p0 / kXaBlock;
+    const int cnt = xa_cnt[(static_cast<int64_t>(b) * Hkv + kvh) * xa_nqb + i];
+    cost = 2 * cnt - (2 * i + 1 > p1 / kBlock ? 1 : 0);
+  } else {
+    cost = key_range(mode, p0 / kBlock, p1 / kBlock, n_sink, seq_w[b]).count();
+  }
   Item it;
   it.b = b;
   it.kvh = kvh;
@@ -180,6 +190,15 @@ Workspace plan_workspace(const Shape& s) {
   w.items_raw = off;   off = align(off + sizeof(Item) * w.max_items);
   w.sort_tmp = off;    off = align(off + sort_tmp);
   w.sort_tmp_bytes = sort_tmp;
+  w.xa_nqb = (s.max_seqlen + kXaBlock - 1) / kXaBlock;
+  w.xa_cnt = off;
+  w.xa_list = off;
+  if (s.xa) {
+    const int64_t rows = static_cast<int64_t>(s.B) * s.Hkv;
+    off = align(off + sizeof(int32_t) * rows * w.xa_nqb);
+    w.xa_list = off;
+    off = align(off + sizeof(int32_t) * rows * xa_row_offset(w.xa_nqb));
+  }
   w.total = off;
   return w;
 }
@@ -197,9 +216,10 @@ hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* mode
   hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(kScanThreads), 0, st, cu, s.B, s.BMq, g.n_sink,
                      g.window_blocks, g.keep_fraction, plan_stamp(s), meta, tile_prefix, seq_w);
   const unsigned grid = static_cast<unsigned>((ws.max_items + 255) / 256);
+  const int32_t* xa_cnt = s.xa ? reinterpret_cast<const int32_t*>(base + ws.xa_cnt) : nullptr;
   hipLaunchKernelGGL(items_kernel, dim3(grid), dim3(256), 0, st, cu, modes, s.B, s.Hkv, s.BMq,
-                     s.parts, g.n_sink, meta, tile_prefix, seq_w, ws.nbins, ws.max_items, raw,
-                     keys_in, vals_in);
+                     s.parts, s.head_config, g.n_sink, meta, tile_prefix, seq_w, xa_cnt,
+                     ws.xa_nqb, ws.nbins, ws.max_items, raw, keys_in, vals_in);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t tmp_bytes = ws.sort_tmp_bytes;

@@ -1,0 +1,391 @@
+// XAttention (XA) block selection for the XA heads of the hybrid prefill.
+//
+// Pages: "Elastic Attention: Test-time Adaptive Sparsity Ratios for Efficient
+// Transformers" runs retrieval or sparse heads in XAttention mode (experimental
+// setup, baselines paragraph: threshold tau = 0.9, XAttention's other settings
+// at their defaults; head configurations FA-XA and XA-SSA).  The selection
+// restates "XAttention: Block Sparse Attention with Antidiagonal Scoring"
+// (method section) at its default block 128 and stride 8:
+//
+//   group score   sum_t <q[aS + S-1-t], k[cS + t]> over the antidiagonal of
+//                 the S x S tile of position groups a (queries) and c (keys),
+//                 positions past the sequence end reading as zero;
+//   softmax       of score * scale / S over the groups c <= a of row a;
+//   block mass    A[i][j] = sum of those probabilities over the 16 x 16 group
+//                 tile of XA query block i and key block j;
+//   selection     block 0 and block i, then blocks in decreasing mass (ties
+//                 to the lower index) until the kept mass reaches tau times
+//                 the row total.
+//
+// One workgroup per (sequence, KV head, XA query block i), 4 waves, the KV
+// group's query heads taken 4 at a time (one per wave).  A wave keeps its
+// head's 16 group rows of block i in registers as the A operand of
+// 16x16x32 bf16 MFMAs: the contraction runs over the S * d values of a group
+// (S query rows in reversed order, d dims each), so one 16 x 16 tile of group
+// scores is S d / 32 MFMAs.  Key blocks j = 0..i stream through LDS (128 key
+// rows, the 8 rows of each group contiguous and groups padded by 16 bytes, so
+// that the 16 columns of a B operand read start on distinct bank groups and
+// every read is one base register plus an immediate offset), staged through
+// registers one block ahead.  The key blocks are walked twice: first for each group row's running
+// max and sum (online, per lane, merged over the 16 lanes of a row at the
+// end), then for the block masses, exp2(x - lse2) summed over the tile.
+// The selection then runs in the same workgroup over its LDS row of masses: a
+// bitonic sort of the candidates (mass bits above the inverted block index,
+// so equal masses keep ascending index), a prefix sum in sorted order and the
+// threshold test in float32.  The per-head keep flags of the KV group are
+// OR-ed into one mask per key block, and the kept blocks are written as one
+// ascending list of (j | head mask << 16) for the attention kernel, which
+// walks the union once and masks each head to its own blocks.
+#include "ea_internal.h"
+
+#include <math.h>
+
+namespace ea {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXaThreads = 256;
+constexpr int kXaWaves = kXaThreads / 64;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kMinusBig = -1.0e30f;
+// word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data, no swizzle)
+constexpr int kBufferWord3 = 0x00020000;
+
+struct XaArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const int8_t* modes;
+  const int32_t* cu;
+  int32_t* cnt;     // [B * Hkv * nqb]
+  int32_t* list;    // [B * Hkv * xa_row_offset(nqb)]
+  float* mass;      // [B, Hq, nqb, nqb] or null
+  uint8_t* keep;    // [B, Hq, nqb, nqb] or null
+  int32_t B, Hq, Hkv, G, nqb, head_config;
+  int32_t region0;  // bytes of the K tile / sort region at the start of LDS
+  float cs;         // softmax scale * log2(e) / S
+  float tau;
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum of one value per thread over the workgroup (red: kXaWaves floats).
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kXaWaves; ++w) s += red[w];
+  return s;
+}
+
+// Exclusive prefix over the workgroup of one value per thread, in thread
+// order (red: kXaWaves + 1 floats); returns the prefix, *total the sum.
+template <typename T>
+__device__ T block_exclusive(T v, T* red, T* total) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  T x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  T before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kXaWaves; ++w) {
+    if (w < wave) before += red[w];
+    all += red[w];
+  }
+  *total = all;
+  return before + x - v;
+}
+
+template <int D>
+__global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
+  constexpr int S = kXaStride;
+  constexpr int KS = S * D / 32;                     // 32-wide k-steps of one group
+  constexpr int CPR = D / 8;                         // 16-byte chunks per key row
+  constexpr int NCH = kXaBlock * CPR / kXaThreads;   // chunks per thread per key tile
+  constexpr int KGS = S * D + 8;                     // elements per padded key group
+  static_assert(NCH * kXaThreads == kXaBlock * CPR, "key tile must split evenly");
+  static_assert((kXaThreads / CPR) % S == 0, "a load round covers whole key groups");
+  static_assert(kXaGroupsPerBlock == 16, "one 16-row MFMA tile of groups per XA block");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);            // key tile, then sort keys
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
+  float* mass_l = reinterpret_cast<float*>(smem + a.region0);  // [kXaWaves][nqb]
+  uint32_t* hm = reinterpret_cast<uint32_t*>(mass_l + kXaWaves * a.nqb);  // [nqb]
+  float* redf = reinterpret_cast<float*>(hm + a.nqb);          // [kXaWaves + 1]
+  int32_t* redi = reinterpret_cast<int32_t*>(redf + kXaWaves + 1);
+
+  // block -> (sequence, KV head, query block), the costliest (largest i) first
+  const int64_t rows = static_cast<int64_t>(a.B) * a.Hkv;
+  const int i = a.nqb - 1 - static_cast<int>(blockIdx.x / rows);
+  const int bk = static_cast<int>(blockIdx.x % rows);
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int tok0 = a.cu[b];
+  const int L = a.cu[b + 1] - tok0;
+  if (static_cast<int64_t>(i) * kXaBlock >= L) return;
+  if (computation_mode(a.head_config, a.modes[bk] != 0) != kModeXA) return;
+  const int ng = (L + S - 1) / S;  // position groups of the sequence
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int r = lane % 16, kq = lane / 16;
+  for (int j = tid; j <= i; j += kXaThreads) hm[j] = 0u;
+
+  // Key rows of block j through a buffer resource that ends at the sequence
+  // end (rows past it read as zeros; the whole offset is in the range-checked
+  // vector offset): thread tid loads chunk tid % CPR of rows
+  // tid / CPR + n (kXaThreads / CPR), n < NCH.
+  constexpr int RPN = kXaThreads / CPR;  // rows per load round
+  const int rs2 = a.Hkv * D * 2;         // bytes between key rows
+  const int koff = (tid / CPR) * rs2 + (tid % CPR) * 16;
+  const uint16_t* kseq = a.K + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
+  u32x4 kreg[NCH];
+  auto kfetch = [&](int j) {
+    const int key0 = j * kXaBlock;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kseq + static_cast<int64_t>(key0) * a.Hkv * D), 0,
+        static_cast<unsigned>(L - key0) * static_cast<unsigned>(rs2), kBufferWord3);
+#pragma unroll
+    for (int n = 0; n < NCH; ++n)
+      kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, koff + n * RPN * rs2, 0, 0));
+  };
+  // LDS: the 8 rows of one key group are contiguous, groups padded by 16
+  // bytes, so the 16 groups a B operand read touches start on 16 distinct
+  // 16-byte bank groups
+  const int kst = (tid / CPR / S) * KGS + ((tid / CPR) % S) * D + (tid % CPR) * 8;
+  auto kstore = [&]() {
+#pragma unroll
+    for (int n = 0; n < NCH; ++n)
+      *reinterpret_cast<u32x4*>(Kt + kst + n * (RPN / S) * KGS) = kreg[n];
+  };
+
+  for (int g0 = 0; g0 < a.G; g0 += kXaWaves) {
+    const int gg = g0 + wave;
+    const bool hv = gg < a.G;
+    const int hq = kvh * a.G + gg;
+    // A operand: group row 16 i + r, contraction index 32 kk + 8 kq + e =
+    // t D + dim, i.e. query position (16 i + r) S + S-1-t
+    bf16x8 qa[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int t = (32 * kk) / D, dim = (32 * kk) % D + 8 * kq;
+      const int p = (16 * i + r) * S + S - 1 - t;
+      qa[kk] = (hv && p < L) ? *reinterpret_cast<const bf16x8*>(
+                                   a.Q + (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + dim)
+                             : bf16x8{};
+    }
+    // lane holds group rows 16 i + 4 kq + e (e = 0..3) of the score tile
+    float lse2[4];
+    for (int pass = 0; pass < 2; ++pass) {
+      float m_e[4], l_e[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m_e[e] = kMinusBig;
+        l_e[e] = 0.f;
+      }
+      kfetch(0);
+      for (int j = 0; j <= i; ++j) {
+        __syncthreads();  // the previous tile (or sort keys) fully read
+        kstore();
+        __syncthreads();
+        if (j < i) kfetch(j + 1);
+        if (!hv) continue;
+        f32x4 s = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          // B operand: key group column r (positions (16 j + r) S + t), same k-slice
+          // group r, row t, dims 32 kk % D + 8 kq: element r KGS + 32 kk + 8 kq
+          s = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(Kt + r * KGS + 32 * kk + 8 * kq), s);
+        }
+        const int c = 16 * j + r;  // this lane's key group
+        if (pass == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ag = 16 * i + 4 * kq + e;
+            const float x = (c <= ag && ag < ng) ? s[e] * a.cs : -INFINITY;
+            const float mn = fmaxf(m_e[e], x);
+            l_e[e] = l_e[e] * __builtin_amdgcn_exp2f(m_e[e] - mn) + __builtin_amdgcn_exp2f(x - mn);
+            m_e[e] = mn;
+          }
+        } else {
+          float ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ag = 16 * i + 4 * kq + e;
+            if (c <= ag && ag < ng) ps += __builtin_amdgcn_exp2f(s[e] * a.cs - lse2[e]);
+          }
+          ps = wave_sum(ps);
+          if (lane == 0) {
+            mass_l[wave * a.nqb + j] = ps;
+            if (a.mass)
+              a.mass[((static_cast<int64_t>(b) * a.Hq + hq) * a.nqb + i) * a.nqb + j] = ps;
+          }
+        }
+      }
+      if (pass == 0) {
+        // merge the 16 lanes that share a group row
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float M = m_e[e];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+          float l = l_e[e] * __builtin_amdgcn_exp2f(m_e[e] - M);
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off, 64);
+          lse2[e] = M + __log2f(l);
+        }
+      }
+    }
+    __syncthreads();  // this quad's masses complete; the key tile is free
+
+    // Threshold selection of each head of the quad, the whole workgroup at a time.
+    for (int w = 0; w < kXaWaves && g0 + w < a.G; ++w) {
+      const float* mrow = mass_l + w * a.nqb;
+      const uint32_t bit = 1u << (g0 + w);
+      float part = 0.f;
+      for (int j = tid; j <= i; j += kXaThreads) part += mrow[j];
+      const float total = block_sum(part, redf);
+      const float target = a.tau * total;
+      const float forced = i > 0 ? mrow[0] + mrow[i] : mrow[0];
+      const int m = i - 1;  // candidates: blocks 1 .. i-1
+      int P2 = 1;
+      while (P2 < m) P2 <<= 1;
+      if (m > 0) {
+        for (int p = tid; p < P2; p += kXaThreads) {
+          const int j = p + 1;
+          keys[p] = p < m ? (static_cast<uint64_t>(__float_as_uint(mrow[j])) << 32) |
+                                static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(j))
+                          : 0ull;
+        }
+        __syncthreads();
+        // bitonic sort, descending
+        for (int k = 2; k <= P2; k <<= 1) {
+          for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            for (int p = tid; p < P2; p += kXaThreads) {
+              const int q = p ^ jj;
+              if (q > p) {
+                const uint64_t x0 = keys[p], x1 = keys[q];
+                const bool desc = (p & k) == 0;
+                if (desc ? (x0 < x1) : (x0 > x1)) {
+                  keys[p] = x1;
+                  keys[q] = x0;
+                }
+              }
+            }
+            __syncthreads();
+          }
+        }
+        // exclusive prefix of the sorted masses; keep entry p while the mass
+        // kept before it is still short of the target
+        const int per = (P2 + kXaThreads - 1) / kXaThreads;
+        const int p0 = tid * per;
+        float mine = 0.f;
+        for (int p = p0; p < min(p0 + per, m); ++p) mine += __uint_as_float(static_cast<uint32_t>(keys[p] >> 32));
+        float all;
+        float before = block_exclusive(mine, redf, &all);
+        for (int p = p0; p < min(p0 + per, m); ++p) {
+          const float v = __uint_as_float(static_cast<uint32_t>(keys[p] >> 32));
+          if (forced + before < target) {
+            const int j = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(keys[p]));
+            hm[j] |= bit;
+          }
+          before += v;
+        }
+      }
+      if (tid == 0) {
+        hm[0] |= bit;
+        hm[i] |= bit;
+      }
+      __syncthreads();
+      if (a.keep) {
+        uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + kvh * a.G + g0 + w) * a.nqb + i) * a.nqb;
+        for (int j = tid; j <= i; j += kXaThreads) krow[j] = (hm[j] & bit) ? 1 : 0;
+      }
+    }
+  }
+
+  // Ascending list of the key blocks some head of the group keeps.
+  __syncthreads();
+  const int per = (i + 1 + kXaThreads - 1) / kXaThreads;
+  const int j0 = tid * per;
+  int32_t mine = 0;
+  for (int j = j0; j < min(j0 + per, i + 1); ++j) mine += hm[j] != 0u;
+  int32_t count;
+  int32_t pos = block_exclusive(mine, redi, &count);
+  int32_t* lrow = a.list + static_cast<int64_t>(bk) * xa_row_offset(a.nqb) + xa_row_offset(i);
+  for (int j = j0; j < min(j0 + per, i + 1); ++j) {
+    if (hm[j] != 0u) lrow[pos++] = j | static_cast<int32_t>(hm[j] << 16);
+  }
+  if (tid == 0) a.cnt[static_cast<int64_t>(bk) * a.nqb + i] = count;
+}
+
+}  // namespace
+
+size_t xa_plan_lds_bytes(const Shape& s) {
+  const int nqb = (s.max_seqlen + kXaBlock - 1) / kXaBlock;
+  if (nqb > 4096) return 0;
+  int P2 = 1;
+  while (P2 < nqb) P2 <<= 1;
+  const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + 8) * 2;
+  const size_t region0 = ktile > 8u * P2 ? ktile : 8u * P2;
+  const size_t bytes = region0 + sizeof(float) * kXaWaves * nqb + sizeof(uint32_t) * nqb +
+                       sizeof(float) * (2 * kXaWaves + 2);
+  return bytes <= 160u * 1024u ? bytes : 0;
+}
+
+hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const void* Q,
+                          const void* K, const int8_t* modes, const int32_t* cu,
+                          const Workspace& ws, char* base, float* mass, uint8_t* keep,
+                          hipStream_t st) {
+  XaArgs a;
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.modes = modes;
+  a.cu = cu;
+  a.cnt = reinterpret_cast<int32_t*>(base + ws.xa_cnt);
+  a.list = reinterpret_cast<int32_t*>(base + ws.xa_list);
+  a.mass = mass;
+  a.keep = keep;
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.nqb = ws.xa_nqb;
+  a.head_config = s.head_config;
+  int P2 = 1;
+  while (P2 < a.nqb) P2 <<= 1;
+  const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + 8) * 2;
+  a.region0 = static_cast<int32_t>(ktile > 8u * P2 ? ktile : 8u * P2);
+  a.cs = g.scale * kLog2e / kXaStride;
+  a.tau = tau;
+  const size_t lds = xa_plan_lds_bytes(s);
+  if (lds == 0) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.nqb) * s.B * s.Hkv);
+  const void* fn = s.d == 128 ? reinterpret_cast<const void*>(&xa_plan_kernel<128>)
+                               : reinterpret_cast<const void*>(&xa_plan_kernel<64>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  if (s.d == 128) hipLaunchKernelGGL(xa_plan_kernel<128>, dim3(grid), dim3(kXaThreads), lds, st, a);
+  else hipLaunchKernelGGL(xa_plan_kernel<64>, dim3(grid), dim3(kXaThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ea

@@ -351,6 +351,82 @@ ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes,
                          void* O, float* lse, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* ---- XAttention head mode -------------------------------------------------
+ *
+ * The pages also run heads in XAttention (XA) mode: a head configuration
+ * "{retrieval-head mode}-{sparse-head mode}" maps the router's decision 0
+ * (retrieval head) and 1 (sparse head) to computation modes, FA-SSA being the
+ * routed prefill above, FA-XA and XA-SSA the two with XA heads, with
+ * XAttention's threshold tau = 0.9 and its other settings at their defaults
+ * (paper body: experimental setup, baselines paragraph; its efficiency
+ * summary quotes the largest prefill speedup for XA-SSA).  XAttention itself
+ * ("XAttention: Block Sparse Attention with Antidiagonal Scoring", method
+ * section) picks, per query head and per query block of `block` tokens, the
+ * key blocks an XA head attends to:
+ *
+ *   1. score every pair of stride-S position groups by the sum over the
+ *      antidiagonal of their S x S tile of Q K^T,
+ *      sum_t <q[aS + S-1-t], k[cS + t]>, positions past the sequence end
+ *      reading as zero;
+ *   2. scale by softmax_scale / S, mask groups after the query group, softmax
+ *      over each group row;
+ *   3. sum those probabilities inside each block x block tile (block mass);
+ *   4. keep block 0 and the diagonal block, then further key blocks in
+ *      decreasing mass (ties to the lower index) until the kept mass reaches
+ *      tau times the row's total.
+ *
+ * An XA head then attends causally to the keys of its kept blocks. */
+typedef enum {
+  EA_HEADS_FA_SSA = 0, /* decision 0 -> FA, 1 -> SA (sink + window) */
+  EA_HEADS_FA_XA = 1,  /* decision 0 -> FA, 1 -> XA */
+  EA_HEADS_XA_SSA = 2  /* decision 0 -> XA, 1 -> SA */
+} ea_head_config;
+
+/* XAttention settings.
+ *   block        XA block edge in tokens; must be 128 (XAttention's default)
+ *   stride       antidiagonal stride S; must be 8 (XAttention's default)
+ *   threshold    tau in [0, 1]
+ *   head_config  an ea_head_config value */
+typedef struct {
+  int32_t block;
+  int32_t stride;
+  float threshold;
+  int32_t head_config;
+} ea_xa_params;
+
+/* Bytes of device workspace ea_xa_prefill needs (0 if the sizes are invalid):
+ * the routed prefill's work list plus, per (sequence, KV head, query block),
+ * a count and the list of kept key blocks (a triangular array of int32). */
+size_t ea_xa_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                    int32_t Hq, int32_t Hkv, int32_t head_dim, ea_dtype dtype);
+
+/* ea_xa_prefill - hybrid prefill with FA, SA and XA heads in one fused
+ * attention launch.
+ *
+ * Arguments as for ea_hybrid_prefill, plus:
+ *   xa        XAttention settings (host struct)
+ *   xa_mass   out float32 [B, Hq, nqb, nqb] block masses of step 3 for the
+ *             XA heads (nqb = ceil(max_seqlen / block); row i holds key
+ *             blocks 0..i of query block i, the rest untouched), or NULL
+ *   xa_keep   out uint8 [B, Hq, nqb, nqb]: 1 where step 4 keeps key block j
+ *             for query block i, 0 for the other j <= i; or NULL
+ *
+ * Rows of heads that are not XA, and rows past a sequence's last block, are
+ * left untouched in xa_mass and xa_keep.  The selection is made per query
+ * head; the attention kernel walks the union of a KV group's kept blocks and
+ * masks each head to its own.  The masses are accumulated in float32 and the
+ * threshold decision is taken in float32.  dtype must be EA_BF16; head_dim 64
+ * or 128; Hq / Hkv <= 16 and a power of two >= 2 (a query tile then lies
+ * inside one XA block); nqb <= 4096.  Work per XA query block grows with its
+ * index (every earlier key block is scored twice: once for the group-row
+ * softmax statistics, once for the masses). */
+ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                        const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                        int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                        int32_t head_dim, const ea_sparsity_params* params,
+                        const ea_xa_params* xa, void* O, float* lse, float* xa_mass,
+                        uint8_t* xa_keep, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ea_mfma_probe - measurement helper, not part of the attention path: the
  * practical bf16 matrix-core ceiling that the attention kernel's throughput is
  * set against beside the data-sheet peak (256 CUs x 2.4 GHz x 4096 FLOP/clk).

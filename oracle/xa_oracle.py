@@ -114,6 +114,36 @@ def block_mass(q: np.ndarray, k: np.ndarray, *, block: int = 128, stride: int = 
     return A
 
 
+def block_mass_rows(q: np.ndarray, k: np.ndarray, rows, *, block: int = 128, stride: int = 8,
+                    scale: float | None = None) -> np.ndarray:
+    """Rows ``rows`` (query blocks) of ``block_mass`` without forming the whole
+    group score matrix: the same three steps restricted to the group rows of
+    those blocks.  Returns [len(rows), nb]."""
+    L, d = q.shape
+    S = int(stride)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = -(-L // S)
+    nb = -(-L // block)
+    R = block // S
+    qp = np.zeros((n * S, d))
+    kp = np.zeros((n * S, d))
+    qp[:L] = np.asarray(q, np.float64)
+    kp[:L] = np.asarray(k, np.float64)
+    out = np.zeros((len(rows), nb))
+    for ri, i in enumerate(rows):
+        a = np.arange(i * R, min((i + 1) * R, n))
+        D = np.zeros((len(a), n))
+        for t in range(S):
+            D += qp[a * S + S - 1 - t] @ kp[t::S].T
+        logits = np.where(np.arange(n)[None, :] <= a[:, None], D * (scale / S), -np.inf)
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        for j in range(i + 1):
+            out[ri, j] = p[:, j * R:(j + 1) * R].sum()
+    return out
+
+
 def select_row(mass_row: np.ndarray, i: int, tau: float) -> np.ndarray:
     """Step 4 for query block i: bool [i + 1] of kept key blocks."""
     a = np.asarray(mass_row[:i + 1], np.float64)

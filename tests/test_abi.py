@@ -21,7 +21,8 @@ def test_every_header_function_is_exported():
                           "ea_kvcache_bytes", "ea_kvcache_init", "ea_kvcache_prefill",
                           "ea_decode_workspace_size", "ea_decode_step",
                           "ea_hybrid_backward_workspace_size", "ea_hybrid_backward",
-                          "ea_router_logit_grad_workspace_size", "ea_router_logit_grad"}
+                          "ea_router_logit_grad_workspace_size", "ea_router_logit_grad",
+                          "ea_xa_prefill_workspace_size", "ea_xa_prefill"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -288,3 +289,42 @@ def test_backward_host_errors():
     assert call(O=None) == -1
     assert call(dQ=A + 8) == -1 and "16-byte" in ea.ea_last_error()
     assert call(ws_bytes=ws - 1) == -3
+
+
+def test_xa_workspace_holds_the_selection_lists():
+    one = ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
+    xa = ea.ea_xa_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
+    nqb = 131072 // 128
+    # counts [Hkv, nqb] and the triangular lists [Hkv, nqb (nqb + 1) / 2] of int32
+    need = 4 * 8 * nqb + 4 * 8 * nqb * (nqb + 1) // 2
+    assert need <= xa - one <= need + 1024
+    assert ea.ea_xa_prefill_workspace_size(1, 1000, 1000, 30, 8, 128, 1) == 0
+
+
+def test_xa_prefill_host_errors():
+    L = ea.lib()
+    A = FAKE
+
+    def call(dtype=1, Hq=8, Hkv=2, d=128, T=1000, max_seqlen=1000, xa=(128, 8, 0.9, 2),
+             ws_bytes=1 << 40, modes=A, O=A):
+        sp = bnd.SparsityParams(64, 1, 0, 0.2, 0.0)
+        xp = None if xa is None else ctypes.byref(bnd.XAParams(*xa))
+        return L.ea_xa_prefill(A, A, A, dtype, modes, A, 1, T, max_seqlen, Hq, Hkv, d,
+                               ctypes.byref(sp), xp, O, None, None, None, A, ws_bytes, None)
+
+    assert call(xa=None) == -1 and "null XA" in ea.ea_last_error()
+    assert call(xa=(64, 8, 0.9, 2)) == -2 and "block" in ea.ea_last_error()
+    assert call(xa=(128, 16, 0.9, 2)) == -2 and "stride" in ea.ea_last_error()
+    assert call(xa=(128, 8, 1.5, 2)) == -1 and "threshold" in ea.ea_last_error()
+    assert call(xa=(128, 8, float("nan"), 2)) == -1
+    assert call(xa=(128, 8, 0.9, 3)) == -1 and "head configuration" in ea.ea_last_error()
+    assert call(dtype=0) == -2 and "EA_BF16" in ea.ea_last_error()
+    assert call(Hq=2, Hkv=2) == -2 and "power of two" in ea.ea_last_error()
+    assert call(Hq=24, Hkv=2) == -2
+    assert call(Hq=64, Hkv=2, d=64) == -2
+    assert call(T=600000, max_seqlen=600000, Hq=4, Hkv=2, d=64) == -2 and "too long" in ea.ea_last_error()
+    assert call(modes=None) == -1
+    assert call(O=None) == -1
+    assert call(ws_bytes=16) == -3
+    # zero tokens launch nothing
+    assert call(T=0, max_seqlen=0) == 0

@@ -229,3 +229,13 @@ def test_xa_effective_flops_counts_selected_pairs():
     got = xa.xa_effective_flops(cm, cu, 4, 2, 8, plan, window_blocks=1)
     fa = orc.effective_flops(np.array([[0, 1]]), cu, 4, 2, 8, window_blocks=1)
     assert got == fa
+
+
+def test_block_mass_rows_is_block_mass():
+    # the row-restricted form used at full size agrees with the whole matrix
+    L, d = 700, 8
+    q, k = _rand(60, L, d), _rand(61, L, d)
+    A = xa.block_mass(q, k, block=64, stride=8)
+    rows = [0, 3, 10]
+    np.testing.assert_allclose(xa.block_mass_rows(q, k, rows, block=64, stride=8), A[rows],
+                               rtol=1e-12, atol=1e-15)

@@ -27,8 +27,9 @@ from .configs import Workload
 STREAM = {
     "q": 1, "k": 2, "v": 3, "lowrank_a": 4, "lowrank_b": 5,
     "w1": 6, "b1": 7, "w2": 8, "b2": 9, "w3": 10, "b3": 11, "w4": 12, "b4": 13,
-    "lengths": 14, "heads": 15, "gumbel": 16,
+    "lengths": 14, "heads": 15, "gumbel": 16, "hitter_dir": 17, "hitter_blocks": 18,
 }
+HITTER_BLOCK = 128
 CHUNK_ROWS = 4096
 CONTROL_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "route_control.json")
 
@@ -199,8 +200,9 @@ def _cu(lengths) -> np.ndarray:
     return cu.astype(np.int32)
 
 
-def _make_k(seed, T, Hkv, d, std, lowrank, cu, shift, out_dtype):
-    """K = std*N(0,1) [+ A B^T low-rank term per head] [+ per-(seq, head) offset]."""
+def _make_k(seed, T, Hkv, d, std, lowrank, cu, shift, out_dtype, extra=None):
+    """K = std*N(0,1) [+ A B^T low-rank term per head] [+ per-(seq, head) offset]
+    [+ whatever ``extra(x, r0)`` adds]."""
     lr_b = None
     if lowrank:
         # B: [Hkv, d, r] ~ N(0, 1/r) so the low-rank term has unit variance per element.
@@ -216,24 +218,65 @@ def _make_k(seed, T, Hkv, d, std, lowrank, cu, shift, out_dtype):
         if shift is not None:
             seg = np.searchsorted(cu, np.arange(r0, r0 + n), side="right") - 1
             x += shift[seg]
+        if extra is not None:
+            extra(x, r0)
 
     return _draw_rows(seed, STREAM["k"], T, (Hkv, d), std, out_dtype, post)
+
+
+def hitter_layout(seed, lengths, Hkv, d, frac, pool_len=100):
+    """Heavy-hitter structure: a unit direction per KV head, and the
+    sequence-local 128-token key blocks that carry it (each with probability
+    ``frac``, never a block holding one of the first or last ``pool_len``
+    tokens, so the router's pooled keys are untouched).  Returns
+    (u float32 [Hkv, d], list of bool arrays per sequence)."""
+    u = _rng(seed, STREAM["hitter_dir"]).standard_normal((Hkv, d), dtype=np.float32)
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    blocks = []
+    r = _rng(seed, STREAM["hitter_blocks"])
+    for L in np.asarray(lengths, dtype=np.int64):
+        n = -(-int(L) // HITTER_BLOCK)
+        hb = r.random(n) < frac
+        j = np.arange(n)
+        first_ok = j * HITTER_BLOCK >= pool_len
+        last_ok = (j + 1) * HITTER_BLOCK <= int(L) - pool_len
+        blocks.append(hb & first_ok & last_ok)
+    return u, blocks
 
 
 def custom_case(seed, lengths, Hq, Hkv, d, dtype="bf16", *, task_hidden=None, router_hidden=None,
                 w_std=0.05, q_std=1.0, k_std=1.0, v_std=1.0, lowrank=0, n_sink=1,
                 keep_fraction=0.2, window_blocks=0, pool_len=100, block=64, k_shift=None,
-                b4=None, softmax_scale=0.0, name="custom") -> Case:
+                b4=None, softmax_scale=0.0, hitters=None, name="custom") -> Case:
     """A case of arbitrary shape.  ``k_shift`` is an optional float32 [B, Hkv, d]
-    offset added to every K row of that sequence and head before rounding."""
+    offset added to every K row of that sequence and head before rounding.
+    ``hitters`` = (frac, strength) adds strength * u_g to every query row of
+    KV group g and to the key rows of the heavy-hitter blocks of
+    ``hitter_layout`` (before rounding), so that those blocks draw most of
+    every query's attention."""
     lengths = np.asarray(lengths, dtype=np.int64)
     cu = _cu(lengths)
     T = int(cu[-1])
     task_hidden = task_hidden or 4 * d
     router_hidden = router_hidden or max(2, d // 2)
-    q = _draw_rows(seed, STREAM["q"], T, (Hq, d), q_std, dtype)
+    qpost = kpost = None
+    if hitters is not None:
+        frac, strength = hitters
+        u, hblocks = hitter_layout(seed, lengths, Hkv, d, frac, pool_len)
+        G = Hq // Hkv
+        uq = np.float32(strength) * np.repeat(u, G, axis=0)          # [Hq, d]
+        hit = np.concatenate([np.repeat(hb, HITTER_BLOCK)[:int(L)]
+                              for hb, L in zip(hblocks, lengths)]) if len(lengths) else np.zeros(0, bool)
+        uk = np.float32(strength) * u                                 # [Hkv, d]
+
+        def qpost(x, r0):
+            x += uq[None]
+
+        def kpost(x, r0):
+            x[hit[r0:r0 + x.shape[0]]] += uk[None]
+    q = _draw_rows(seed, STREAM["q"], T, (Hq, d), q_std, dtype, qpost)
     k = _make_k(seed, T, Hkv, d, k_std, lowrank, cu,
-                None if k_shift is None else np.asarray(k_shift, dtype=np.float32), dtype)
+                None if k_shift is None else np.asarray(k_shift, dtype=np.float32), dtype, kpost)
     v = _draw_rows(seed, STREAM["v"], T, (Hkv, d), v_std, dtype)
     w = draw_router_weights(seed, d, task_hidden, router_hidden, w_std)
     if b4 is not None:
@@ -251,7 +294,8 @@ def workload_lengths(wl: Workload, seed: int) -> np.ndarray:
     return draw_lengths(seed, wl.n_seqs, lo, hi)
 
 
-def build_case(wl: Workload, seed: int | None = None, *, control: bool = True) -> Case:
+def build_case(wl: Workload, seed: int | None = None, *, control: bool = True,
+               hitters=None) -> Case:
     """The seeded inputs of workload ``wl``.
 
     With ``control`` the stored routing controls (seed actually used, final
@@ -278,7 +322,7 @@ def build_case(wl: Workload, seed: int | None = None, *, control: bool = True) -
                     router_hidden=wl.router_hidden, w_std=wl.w_std, q_std=wl.q_std,
                     k_std=wl.k_std, v_std=wl.v_std, lowrank=wl.lowrank, n_sink=wl.n_sink,
                     keep_fraction=wl.keep_fraction, pool_len=wl.pool_len, block=wl.block,
-                    k_shift=shift, b4=b4, name=wl.name)
+                    k_shift=shift, b4=b4, hitters=hitters, name=wl.name)
     if target is None and wl.sa_heads is not None:
         target = draw_sa_heads(seed, wl.sa_heads, wl.Hkv)
     c.target_modes = target
