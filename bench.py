@@ -479,6 +479,185 @@ def bench_backward(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_xa(c, cmodes, budget_s=12.0):
+    """The oracle's XA path on a bounded sample of the layer: for XA query
+    heads at seeded query blocks, the block masses of that block row, its
+    selection, and the attention of its 128 rows over the kept blocks, until
+    ~budget_s of CPU time is spent; the sample's computed-block FLOPs over its
+    wall time."""
+    from oracle import xa_oracle as xo
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    from workloads import gen
+    rng = np.random.default_rng(0)
+    G = c.Hq // c.Hkv
+    L = int(c.lengths[0])
+    nb = -(-L // 128)
+    xa_heads = [hq for hq in range(c.Hq) if cmodes[0, hq // G] == xo.MODE_XA]
+    qh = {hq: gen.bf16_bits_to_f32(np.ascontiguousarray(c.q[:, hq])) for hq in xa_heads[:2]}
+    kh = {g: gen.bf16_bits_to_f32(np.ascontiguousarray(c.k[:, g])) for g in {h // G for h in qh}}
+    vh = {g: gen.bf16_bits_to_f32(np.ascontiguousarray(c.v[:, g])) for g in kh}
+    done_flops, units, t_used = 0, 0, 0.0
+    while t_used < budget_s and units < 256:
+        hq = list(qh)[units % len(qh)]
+        g = hq // G
+        i = int(rng.integers(0, nb))
+        t0 = time.perf_counter()
+        A = xo.block_mass_rows(qh[hq], kh[g], [i])
+        keep = xo.select_row(A[0], i, 0.9)
+        rows = np.arange(i * 128, min(L, i * 128 + 128))
+        cols = np.concatenate([np.arange(j * 128, min(L, j * 128 + 128)) for j in np.nonzero(keep)[0]])
+        s_ = (qh[hq][rows].astype(np.float64) @ kh[g][cols].astype(np.float64).T) / np.sqrt(c.d)
+        s_ = np.where(cols[None, :] <= rows[:, None], s_, -np.inf)
+        p = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        _ = (p @ vh[g][cols].astype(np.float64)) / p.sum(axis=1, keepdims=True)
+        t_used += time.perf_counter() - t0
+        done_flops += 4 * c.d * len(rows) * len(cols)
+        units += 1
+    return {
+        "value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{units} XA query blocks of 128 rows x one query head at seeded positions of "
+                  f"{c.name}: block masses of the row, threshold selection, float64 attention "
+                  f"over the kept blocks; FLOPs of the kept blocks; {t_used:.1f} s of CPU; "
+                  f"{platform.machine()} host",
+    }
+
+
+def bench_xa(args):
+    """Hybrid prefill with XAttention heads (one layer): router, XA selection +
+    work list (plan), fused attention (run).  Effective FLOPs count the blocks
+    the heads compute (XA heads: the kept ones).  Also times an all-FA prefill
+    of the same inputs for the speedup over full attention.  Prints one JSON
+    line of its own."""
+    import torch
+
+    import full_attention_long_amd as ea
+    from full_attention_long_amd import metrics
+    from workloads import gen
+    from workloads.configs import WORKLOADS
+    name = args.runs.split(",")[0]
+    hitters = None if args.xa_plain else (0.1, 8.0)
+    log(f"xa {name} {args.xa_config} hitters={hitters}: generating inputs")
+    c = gen.build_case(WORKLOADS[name], hitters=hitters)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    q, k, v = bf(c.q), bf(c.k), bf(c.v)
+    cu = torch.from_numpy(c.cu_seqlens).cuda()
+    w = {n: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda() for n, a in c.weights.items()}
+    maxlen = int(c.lengths.max())
+    O = torch.empty_like(q)
+    lse = torch.empty((c.Hq, c.T), dtype=torch.float32, device="cuda")
+    modes = torch.empty((c.B, c.Hkv), dtype=torch.int8, device="cuda")
+    logits = torch.empty((c.B, c.Hkv, 2), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ea.ea_xa_prefill_workspace_size(c.B, c.T, maxlen, c.Hq, c.Hkv, c.d, 1),
+                     dtype=torch.uint8, device="cuda")
+    xg = dict(head_config=args.xa_config, threshold=args.xa_tau, n_sink=c.n_sink,
+              keep_fraction=c.keep_fraction)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ea.ea_route(k, cu, w, pool_len=c.pool_len, modes=modes, logits=logits)
+        if ev is not None:
+            ev[1].record()
+        ea.ea_xa_prefill_plan(q, k, modes, cu, maxlen, ws, **xg)
+        if ev is not None:
+            ev[2].record()
+        ea.ea_xa_prefill_run(q, k, v, modes, cu, maxlen, ws, out=O, lse=lse, **xg)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    m = modes.cpu().numpy()
+    assert np.array_equal(m, c.target_modes), f"{name}: routing differs from the target"
+    cm = metrics.computation_modes(m, args.xa_config)
+    nqb = -(-maxlen // 128)
+    keep = torch.zeros((c.B, c.Hq, nqb, nqb), dtype=torch.uint8, device="cuda")
+    ea.ea_xa_prefill_plan(q, k, modes, cu, maxlen, ws, keep=keep, **xg)
+    torch.cuda.synchronize()
+    keep_np = keep.cpu().numpy()
+    del keep
+    ef = metrics.xa_effective_flops(cm, keep_np, c.lengths, c.Hq, c.Hkv, c.d, n_sink=c.n_sink,
+                                    keep_fraction=c.keep_fraction)
+    sel_flops = metrics.xa_selection_flops(cm, c.lengths, c.Hq, c.Hkv, c.d)
+    xa_rows = [(b, hq) for b in range(c.B) for hq in range(c.Hq) if cm[b, hq // (c.Hq // c.Hkv)] == 2]
+    tri = sum((-(-int(c.lengths[b]) // 128)) * (-(-int(c.lengths[b]) // 128) + 1) // 2 for b, _ in xa_rows)
+    density = float(sum(int(np.tril(keep_np[b, hq]).sum()) for b, hq in xa_rows)) / max(1, tri)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[E() for _ in range(4)] for _ in range(args.steps)]
+    start, stop = E(), E()
+    torch.cuda.synchronize()
+    start.record()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    stop.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / args.steps
+    seg = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                    for e in evs])
+    route_ms, plan_ms, run_ms = seg.mean(axis=0)
+    # the same inputs under full attention on every head
+    fa_modes = torch.zeros_like(modes)
+    wsf = torch.empty(ea.ea_hybrid_prefill_workspace_size(c.B, c.T, maxlen, c.Hq, c.Hkv, c.d, 1),
+                      dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        ea.ea_hybrid_prefill(q, k, v, fa_modes, cu, maxlen, out=O, lse=lse, workspace=wsf,
+                             n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+    torch.cuda.synchronize()
+    a_, b_ = E(), E()
+    a_.record()
+    n_fa = max(2, args.steps // 4)
+    for _ in range(n_fa):
+        ea.ea_hybrid_prefill(q, k, v, fa_modes, cu, maxlen, out=O, lse=lse, workspace=wsf,
+                             n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+    b_.record()
+    torch.cuda.synchronize()
+    fa_ms = a_.elapsed_time(b_) / n_fa
+    log(f"xa {name} {args.xa_config}: step {step_ms:.3f} ms (route {route_ms:.3f}, selection + "
+        f"list {plan_ms:.3f}, attention {run_ms:.3f}); kept density {density:.3f}; all-FA "
+        f"{fa_ms:.3f} ms -> {fa_ms / step_ms:.2f}x")
+    probe = mfma_probe()
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
+    achieved = ef / (run_ms * 1e-3) / 1e12
+    out = {
+        "metric": "hybrid prefill with XAttention heads at 128K: effective TFLOP/s on the computed "
+                  "blocks, ms/layer, speedup over full attention",
+        "value": round(ef / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}:{args.xa_config}" + ("" if hitters is None else ":hitters"),
+                   "seq_len": maxlen, "Hq": c.Hq, "Hkv": c.Hkv, "d": c.d,
+                   "xa_threshold": args.xa_tau, "xa_block": 128, "xa_stride": 8,
+                   "hitters": None if hitters is None else {"block_fraction": hitters[0],
+                                                            "strength": hitters[1]},
+                   "xa_kv_heads": int((cm == 2).sum()), "sa_kv_heads": int((cm == 1).sum()),
+                   "kept_block_density": round(density, 4), "effective_flops": int(ef),
+                   "route_ms": round(float(route_ms), 4),
+                   "xa_selection_and_list_ms": round(float(plan_ms), 4),
+                   "xa_selection_flops": int(sel_flops),
+                   "xa_selection_tflops": round(sel_flops / (plan_ms * 1e-3) / 1e12, 3),
+                   "attention_ms": round(float(run_ms), 4),
+                   "all_fa_prefill_ms": round(fa_ms, 4),
+                   "speedup_over_full_attention": round(fa_ms / step_ms, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "ea::attention_kernel_bf16<128, true>",
+                     "avg_launch_ms": round(float(run_ms), 4), "flops_per_launch": float(ef),
+                     "mfma_loop_tflops": probe["tflops"],
+                     "frac_of_mfma_loop": round(achieved / probe["tflops"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_xa(c, cm, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def calibrate(mib):
     """One elementwise kernel of known traffic (reads and writes mib MiB), so
     that profiler byte counters can be scaled to bytes."""
@@ -547,6 +726,13 @@ def main():
                     help="measure decode steps over a mode-aware KV cache holding each --runs "
                          "workload as the prompt instead (default qwen4b_s128k_sa2,sa6 and "
                          "varlen8)")
+    ap.add_argument("--xa", action="store_true",
+                    help="measure the prefill with XAttention heads of the first --runs workload "
+                         "instead (default qwen4b_s128k_sa2)")
+    ap.add_argument("--xa-config", default="XA-SSA", choices=["XA-SSA", "FA-XA", "FA-SSA"])
+    ap.add_argument("--xa-tau", type=float, default=0.9, help="XAttention threshold (--xa)")
+    ap.add_argument("--xa-plain", action="store_true",
+                    help="--xa on the workload's plain inputs (no heavy-hitter key blocks)")
     ap.add_argument("--calibrate-mib", type=int, default=0,
                     help="first run one elementwise kernel that reads and writes this many MiB "
                          "(for scaling profiler byte counters)")
@@ -577,6 +763,11 @@ def main():
         if args.runs == ",".join(DEFAULT_RUNS):
             args.runs = "qwen4b_s128k_sa2,qwen4b_s128k_sa6,varlen8"
         bench_decode(args)
+        return
+    if args.xa:
+        if args.runs == ",".join(DEFAULT_RUNS):
+            args.runs = "qwen4b_s128k_sa2"
+        bench_xa(args)
         return
     if args.dual:
         if args.runs == ",".join(DEFAULT_RUNS):

@@ -31,6 +31,8 @@ from .binding import (  # noqa: F401
     ea_router_logit_grad,
     ea_router_logit_grad_workspace_size,
     ea_xa_prefill,
+    ea_xa_prefill_plan,
+    ea_xa_prefill_run,
     ea_xa_prefill_workspace_size,
     header_functions,
     lib,

@@ -127,6 +127,14 @@ def lib() -> ctypes.CDLL:
     L.ea_xa_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                 ctypes.POINTER(SparsityParams), ctypes.POINTER(XAParams), vp, vp,
                                 vp, vp, vp, sz, vp]
+    L.ea_xa_prefill_plan.restype = i32
+    L.ea_xa_prefill_plan.argtypes = [vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                     ctypes.POINTER(SparsityParams), ctypes.POINTER(XAParams), vp,
+                                     vp, vp, sz, vp]
+    L.ea_xa_prefill_run.restype = i32
+    L.ea_xa_prefill_run.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                    ctypes.POINTER(SparsityParams), ctypes.POINTER(XAParams), vp,
+                                    vp, vp, sz, vp]
     L.ea_mfma_probe.restype = i32
     L.ea_mfma_probe.argtypes = [vp, i32, i32, ctypes.c_uint32, ctypes.POINTER(i64), vp]
     _lib = L
@@ -285,7 +293,6 @@ def ea_xa_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, head_config="X
     tensors, nqb = ceil(max_seqlen / xa_block)) receive the XA heads' block
     masses and keep flags when given."""
     import torch
-    cfg = HEAD_CONFIGS[head_config] if isinstance(head_config, str) else int(head_config)
     T, Hq, d = Q.shape
     Hkv = K.shape[1]
     B = cu_seqlens.numel() - 1
@@ -299,11 +306,54 @@ def ea_xa_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, head_config="X
         if t is not None:
             _dev(t, n)
     sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
-    xp = XAParams(xa_block, stride, threshold, cfg)
+    xp = _xa_params(head_config, threshold, xa_block, stride)
     _check(lib().ea_xa_prefill(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes), _ptr(cu_seqlens), B, T,
                                max_seqlen, Hq, Hkv, d, ctypes.byref(sp), ctypes.byref(xp), _ptr(out),
                                _ptr(lse), _ptr(mass), _ptr(keep), _ptr(workspace),
                                workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def _xa_params(head_config, threshold, xa_block, stride):
+    cfg = HEAD_CONFIGS[head_config] if isinstance(head_config, str) else int(head_config)
+    return XAParams(xa_block, stride, threshold, cfg)
+
+
+def ea_xa_prefill_plan(Q, K, modes, cu_seqlens, max_seqlen: int, workspace, *,
+                       head_config="XA-SSA", threshold: float = 0.9, xa_block: int = 128,
+                       stride: int = 8, n_sink: int = 1, window_blocks: int = 0,
+                       keep_fraction: float = 0.2, softmax_scale: float = 0.0, block: int = 64,
+                       mass=None, keep=None, stream=None):
+    """XA selection and work list into ``workspace`` (uint8 device tensor of
+    ``ea_xa_prefill_workspace_size`` bytes)."""
+    for t, n in [(Q, "Q"), (K, "K"), (modes, "modes"), (cu_seqlens, "cu_seqlens"),
+                 (workspace, "workspace")]:
+        _dev(t, n)
+    T, Hq, d = Q.shape
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    xp = _xa_params(head_config, threshold, xa_block, stride)
+    _check(lib().ea_xa_prefill_plan(_ptr(Q), _ptr(K), _dtype_code(Q), _ptr(modes), _ptr(cu_seqlens),
+                                    cu_seqlens.numel() - 1, T, max_seqlen, Hq, K.shape[1], d,
+                                    ctypes.byref(sp), ctypes.byref(xp), _ptr(mass), _ptr(keep),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def ea_xa_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace, *,
+                      head_config="XA-SSA", threshold: float = 0.9, xa_block: int = 128,
+                      stride: int = 8, n_sink: int = 1, window_blocks: int = 0,
+                      keep_fraction: float = 0.2, softmax_scale: float = 0.0, block: int = 64,
+                      out=None, lse=None, with_lse: bool = True, stream=None):
+    """The attention launch over a workspace ``ea_xa_prefill_plan`` filled."""
+    _dev(workspace, "workspace")
+    T, Hq, Hkv, d, B, code, out, lse, workspace = _prefill_args(
+        Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    xp = _xa_params(head_config, threshold, xa_block, stride)
+    _check(lib().ea_xa_prefill_run(_ptr(Q), _ptr(K), _ptr(V), code, _ptr(modes), _ptr(cu_seqlens),
+                                   B, T, max_seqlen, Hq, Hkv, d, ctypes.byref(sp), ctypes.byref(xp),
+                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)))
     return out, lse
 
 

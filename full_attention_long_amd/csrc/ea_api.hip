@@ -262,12 +262,16 @@ size_t ea_xa_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max
   return ea::plan_workspace(s).total;
 }
 
-ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
-                        const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
-                        int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
-                        int32_t head_dim, const ea_sparsity_params* p, const ea_xa_params* xa,
-                        void* O, float* lse, float* xa_mass, uint8_t* xa_keep, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the XA prefill entry points.
+ea_status check_xa(int32_t B, int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                   int32_t head_dim, ea_dtype dtype, const ea_sparsity_params* p,
+                   const ea_xa_params* xa, const void* modes, const void* cu_seqlens,
+                   const void* workspace, size_t workspace_bytes, ea::Shape* s, ea::Workspace* ws,
+                   ea::Geometry* g) {
   if (!xa) return fail(EA_ERR_INVALID_ARG, "null XA params");
   if (xa->block != ea::kXaBlock)
     return fail(EA_ERR_UNSUPPORTED, "XA block must be %d (got %d)", ea::kXaBlock, xa->block);
@@ -278,19 +282,80 @@ ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dt
   if (xa->head_config != EA_HEADS_FA_SSA && xa->head_config != EA_HEADS_FA_XA &&
       xa->head_config != EA_HEADS_XA_SSA)
     return fail(EA_ERR_INVALID_ARG, "unknown head configuration %d", xa->head_config);
-  ea::Shape s;
-  ea::Workspace ws;
-  ea::Geometry g;
   ea_status st = check_prefill(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, modes,
-                               cu_seqlens, workspace, workspace_bytes, &s, &ws, &g, 1,
+                               cu_seqlens, workspace, workspace_bytes, s, ws, g, 1,
                                xa->head_config, 1);
   if (st != EA_OK) return st;
   if (dtype != EA_BF16) return fail(EA_ERR_UNSUPPORTED, "XA mode needs dtype EA_BF16");
-  if (s.G < 2 || s.G > 16 || (s.G & (s.G - 1)) != 0)
-    return fail(EA_ERR_UNSUPPORTED, "XA mode needs Hq / Hkv a power of two in [2, 16] (got %d)", s.G);
-  if (ea::xa_plan_lds_bytes(s) == 0)
+  if (s->G < 2 || s->G > 16 || (s->G & (s->G - 1)) != 0)
+    return fail(EA_ERR_UNSUPPORTED, "XA mode needs Hq / Hkv a power of two in [2, 16] (got %d)", s->G);
+  if (ea::xa_plan_lds_bytes(*s) == 0)
     return fail(EA_ERR_UNSUPPORTED, "max_seqlen %d is too long for XA mode (at most %d blocks of %d)",
                 max_seqlen, 4096, ea::kXaBlock);
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status ea_xa_prefill_plan(const void* Q, const void* K, ea_dtype dtype, const int8_t* modes,
+                             const int32_t* cu_seqlens, int32_t B, int64_t total_tokens,
+                             int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             const ea_sparsity_params* p, const ea_xa_params* xa,
+                             float* xa_mass, uint8_t* xa_keep, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  ea_status st = check_xa(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, xa, modes,
+                          cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
+  if (!Q || !K) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K)) return fail(EA_ERR_INVALID_ARG, "Q and K must be 16-byte aligned");
+  if (total_tokens == 0) return ok();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  hipError_t e = ea::launch_xa_plan(s, g, xa->threshold, Q, K, modes, cu_seqlens, ws, base, xa_mass,
+                                    xa_keep, hs);
+  if (e == hipSuccess) e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "XA plan launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ea_status ea_xa_prefill_run(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                            const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                            int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                            int32_t head_dim, const ea_sparsity_params* p, const ea_xa_params* xa,
+                            void* O, float* lse, const void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  ea_status st = check_xa(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, xa, modes,
+                          cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
+  if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
+  if (total_tokens == 0) return ok();
+  hipError_t e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr},
+                                      ws, static_cast<char*>(const_cast<void*>(workspace)),
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "XA attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                        const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                        int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                        int32_t head_dim, const ea_sparsity_params* p, const ea_xa_params* xa,
+                        void* O, float* lse, float* xa_mass, uint8_t* xa_keep, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  ea::Shape s;
+  ea::Workspace ws;
+  ea::Geometry g;
+  ea_status st = check_xa(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, p, xa, modes,
+                          cu_seqlens, workspace, workspace_bytes, &s, &ws, &g);
+  if (st != EA_OK) return st;
   if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
   if (total_tokens == 0) return ok();
   hipStream_t hs = static_cast<hipStream_t>(stream);

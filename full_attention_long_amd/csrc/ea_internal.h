@@ -114,6 +114,7 @@ __device__ inline bool block_visible(int mode, int kb, int qblk, int ns, int w) 
 enum Meta : int {
   kMetaTiles = 0,       // sum over sequences of ceil(L_b / BMq); items = tiles * Hkv
   kMetaStamp = 1,       // plan_stamp() of the sizes the list was built for
+  kMetaXaRows = 2,      // XA mode: number of (sequence, KV head) rows in XA mode
   kMetaSlots = 64
 };
 
@@ -126,7 +127,7 @@ struct Workspace {
   // XA mode only (Shape.xa): per (sequence, KV head, query block) the number
   // of kept key blocks, and the triangular array of their list entries
   // (key block j | per-head mask << 16, ascending j)
-  size_t xa_cnt, xa_list;
+  size_t xa_cnt, xa_list, xa_rows;
   int32_t xa_nqb;      // query blocks of kXaBlock per sequence (upper bound)
 };
 

@@ -193,11 +193,14 @@ Workspace plan_workspace(const Shape& s) {
   w.xa_nqb = (s.max_seqlen + kXaBlock - 1) / kXaBlock;
   w.xa_cnt = off;
   w.xa_list = off;
+  w.xa_rows = off;
   if (s.xa) {
     const int64_t rows = static_cast<int64_t>(s.B) * s.Hkv;
     off = align(off + sizeof(int32_t) * rows * w.xa_nqb);
     w.xa_list = off;
     off = align(off + sizeof(int32_t) * rows * xa_row_offset(w.xa_nqb));
+    w.xa_rows = off;
+    off = align(off + sizeof(int32_t) * rows);
   }
   w.total = off;
   return w;

@@ -59,11 +59,13 @@ struct XaArgs {
   const uint16_t* K;
   const int8_t* modes;
   const int32_t* cu;
+  const int32_t* meta;   // meta[kMetaXaRows]: number of XA rows
+  const int32_t* rows;   // the XA (sequence, KV head) rows, b * Hkv + kvh
   int32_t* cnt;     // [B * Hkv * nqb]
   int32_t* list;    // [B * Hkv * xa_row_offset(nqb)]
   float* mass;      // [B, Hq, nqb, nqb] or null
   uint8_t* keep;    // [B, Hq, nqb, nqb] or null
-  int32_t B, Hq, Hkv, G, nqb, head_config;
+  int32_t B, Hq, Hkv, G, nqb, nqb_pad, head_config;
   int32_t region0;  // bytes of the K tile / sort region at the start of LDS
   float cs;         // softmax scale * log2(e) / S
   float tau;
@@ -115,6 +117,30 @@ __device__ T block_exclusive(T v, T* red, T* total) {
   return before + x - v;
 }
 
+// The (sequence, KV head) rows whose heads run in XA mode, in order, and
+// their count (one workgroup).
+__global__ __launch_bounds__(kXaThreads) void xa_rows_kernel(const int8_t* __restrict__ modes,
+                                                              const int32_t* __restrict__ cu,
+                                                              int32_t B, int32_t Hkv,
+                                                              int32_t head_config,
+                                                              int32_t* __restrict__ rows,
+                                                              int32_t* __restrict__ meta) {
+  __shared__ int32_t red[kXaWaves + 1];
+  int32_t base = 0;
+  const int n = B * Hkv;
+  for (int r0 = 0; r0 < n; r0 += kXaThreads) {
+    const int r = r0 + static_cast<int>(threadIdx.x);
+    const bool x = r < n && cu[r / Hkv + 1] > cu[r / Hkv] &&
+                   computation_mode(head_config, modes[r] != 0) == kModeXA;
+    int32_t all;
+    const int32_t pos = block_exclusive(static_cast<int32_t>(x), red, &all);
+    if (x) rows[base + pos] = r;
+    base += all;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) meta[kMetaXaRows] = base;
+}
+
 template <int D>
 __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
   constexpr int S = kXaStride;
@@ -134,15 +160,22 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
   float* redf = reinterpret_cast<float*>(hm + a.nqb);          // [kXaWaves + 1]
   int32_t* redi = reinterpret_cast<int32_t*>(redf + kXaWaves + 1);
 
-  // block -> (sequence, KV head, query block), the costliest (largest i) first
-  const int64_t rows = static_cast<int64_t>(a.B) * a.Hkv;
-  const int i = a.nqb - 1 - static_cast<int>(blockIdx.x / rows);
-  const int bk = static_cast<int>(blockIdx.x % rows);
+  // Work item t = the workgroup's position in the XCD-chunked order
+  // (list_position): items run in bands of kXcdChunk query blocks, the
+  // costliest (largest i) band first; inside a band, one XA row after the
+  // other, kXcdChunk consecutive query blocks each, so that the workgroups an
+  // XCD runs together stream the same key blocks through its L2.
+  const int64_t t = list_position(blockIdx.x);
+  const int n_rows = a.meta[kMetaXaRows];
+  if (t >= static_cast<int64_t>(n_rows) * a.nqb_pad) return;
+  const int64_t band = t / (static_cast<int64_t>(kXcdChunk) * n_rows);
+  const int rem = static_cast<int>(t - band * kXcdChunk * n_rows);
+  const int bk = a.rows[rem / kXcdChunk];
+  const int i = a.nqb_pad - 1 - static_cast<int>(band * kXcdChunk + rem % kXcdChunk);
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  if (static_cast<int64_t>(i) * kXaBlock >= L) return;
-  if (computation_mode(a.head_config, a.modes[bk] != 0) != kModeXA) return;
+  if (i < 0 || static_cast<int64_t>(i) * kXaBlock >= L) return;
   const int ng = (L + S - 1) / S;  // position groups of the sequence
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -208,13 +241,16 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
         __syncthreads();
         if (j < i) kfetch(j + 1);
         if (!hv) continue;
-        f32x4 s = f32x4{};
+        // B operand: key group column r (positions (16 j + r) S + t), same
+        // k-slice: group r, row t, dims 32 kk % D + 8 kq, i.e. element
+        // r KGS + 32 kk + 8 kq; four independent accumulation chains keep the
+        // matrix pipe busy
+        f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          // B operand: key group column r (positions (16 j + r) S + t), same k-slice
-          // group r, row t, dims 32 kk % D + 8 kq: element r KGS + 32 kk + 8 kq
-          s = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(Kt + r * KGS + 32 * kk + 8 * kq), s);
-        }
+        for (int kk = 0; kk < KS; ++kk)
+          sc[kk & 3] = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(Kt + r * KGS + 32 * kk + 8 * kq),
+                              sc[kk & 3]);
+        const f32x4 s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
         const int c = 16 * j + r;  // this lane's key group
         if (pass == 0) {
 #pragma unroll
@@ -360,6 +396,10 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   a.K = static_cast<const uint16_t*>(K);
   a.modes = modes;
   a.cu = cu;
+  int32_t* meta = reinterpret_cast<int32_t*>(base + ws.meta);
+  int32_t* rows = reinterpret_cast<int32_t*>(base + ws.xa_rows);
+  a.meta = meta;
+  a.rows = rows;
   a.cnt = reinterpret_cast<int32_t*>(base + ws.xa_cnt);
   a.list = reinterpret_cast<int32_t*>(base + ws.xa_list);
   a.mass = mass;
@@ -369,6 +409,7 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   a.Hkv = s.Hkv;
   a.G = s.G;
   a.nqb = ws.xa_nqb;
+  a.nqb_pad = (ws.xa_nqb + kXcdChunk - 1) / kXcdChunk * kXcdChunk;
   a.head_config = s.head_config;
   int P2 = 1;
   while (P2 < a.nqb) P2 <<= 1;
@@ -378,7 +419,13 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   a.tau = tau;
   const size_t lds = xa_plan_lds_bytes(s);
   if (lds == 0) return hipErrorInvalidValue;
-  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.nqb) * s.B * s.Hkv);
+  hipLaunchKernelGGL(xa_rows_kernel, dim3(1), dim3(kXaThreads), 0, st, modes, cu, s.B, s.Hkv,
+                     s.head_config, rows, meta);
+  // one workgroup per (XA row, query block) at most, rounded up to whole
+  // rounds of the XCD-chunked order
+  constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
+  const int64_t items = static_cast<int64_t>(a.nqb_pad) * s.B * s.Hkv;
+  const unsigned grid = static_cast<unsigned>((items + span - 1) / span * span);
   const void* fn = s.d == 128 ? reinterpret_cast<const void*>(&xa_plan_kernel<128>)
                                : reinterpret_cast<const void*>(&xa_plan_kernel<64>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

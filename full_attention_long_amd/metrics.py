@@ -73,3 +73,67 @@ def msr(modes) -> float:
     """Share of (sequence, KV head) pairs routed to sparse attention."""
     m = np.asarray(modes)
     return float((m != 0).mean())
+
+
+XA_BLOCK = 128
+# computation mode (0 FA, 1 SA, 2 XA) of router decisions 0 / 1 per head configuration
+HEAD_CONFIG_MODES = {"FA-SSA": (0, 1), "FA-XA": (0, 2), "XA-SSA": (2, 1)}
+
+
+def computation_modes(modes, config: str) -> np.ndarray:
+    """[B, Hkv] computation modes of router decisions ``modes`` under ``config``."""
+    return np.asarray(HEAD_CONFIG_MODES[config], dtype=np.int64)[np.asarray(modes, dtype=np.int64)]
+
+
+def xa_head_pairs(keep: np.ndarray, L: int) -> int:
+    """Sum of rows * cols over the (64-query block, 64-key block) pairs an XA
+    head computes, given its keep flags ``keep`` [nb, nb] over 128-token blocks
+    (row i: key blocks kept for query block i): causal pairs whose 128-blocks
+    are kept, partly masked ones counted in full."""
+    N = -(-int(L) // BLOCK)
+    size = np.minimum(BLOCK, int(L) - BLOCK * np.arange(N)).astype(np.int64)
+    total = 0
+    for qb in range(N):
+        i = qb // (XA_BLOCK // BLOCK)
+        kb = np.arange(qb + 1)
+        ok = np.asarray(keep[i, kb // (XA_BLOCK // BLOCK)], dtype=bool)
+        total += int(size[qb]) * int(size[kb][ok].sum())
+    return total
+
+
+def xa_effective_flops(cmodes, keep, lengths, Hq: int, Hkv: int, d: int, *, n_sink: int,
+                       keep_fraction: float, window_blocks_: int = 0) -> int:
+    """EF of a layer with FA (0), SA (1) and XA (2) computation modes
+    ``cmodes`` [B, Hkv]; ``keep`` [B, Hq, nqb, nqb] holds the XA heads' keep
+    flags (as written by ea_xa_prefill)."""
+    G = Hq // Hkv
+    total = 0
+    for b, L in enumerate(lengths):
+        L = int(L)
+        if L <= 0:
+            continue
+        w = window_blocks(L, n_sink, keep_fraction, window_blocks_)
+        for g in range(Hkv):
+            m = int(cmodes[b][g])
+            if m == 0:
+                total += G * _pair_sum(L, None)
+            elif m == 1:
+                total += G * _pair_sum(L, n_sink + w)
+            else:
+                for hq in range(g * G, (g + 1) * G):
+                    total += xa_head_pairs(keep[b, hq], L)
+    return 4 * d * total
+
+
+def xa_selection_flops(cmodes, lengths, Hq: int, Hkv: int, d: int, stride: int = 8) -> int:
+    """Matrix FLOPs of the XA selection: per XA query head and query block i,
+    i + 1 key blocks of 16 x 16 group scores over S * d products, scored
+    twice (statistics pass and mass pass)."""
+    G = Hq // Hkv
+    per_tile = 2 * (XA_BLOCK // stride) ** 2 * stride * d
+    total = 0
+    for b, L in enumerate(lengths):
+        nb = -(-int(L) // XA_BLOCK)
+        n_xa = int((np.asarray(cmodes[b]) == 2).sum()) * G
+        total += n_xa * 2 * per_tile * (nb * (nb + 1) // 2)
+    return total

@@ -427,6 +427,29 @@ ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dt
                         const ea_xa_params* xa, void* O, float* lse, float* xa_mass,
                         uint8_t* xa_keep, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ea_xa_prefill_plan / ea_xa_prefill_run - the two halves of ea_xa_prefill.
+ *
+ * plan runs the XA selection of every XA head (reading Q, K, modes and
+ * cu_seqlens; writing xa_mass / xa_keep when given) and builds the
+ * cost-ordered work list, XA items costed by their kept blocks, into
+ * `workspace`; run launches the fused attention over a workspace that plan
+ * filled with the same arguments.  Arguments, limits and errors are those of
+ * ea_xa_prefill; running over a workspace that was not planned for these
+ * arguments is a precondition violation (not detected). */
+ea_status ea_xa_prefill_plan(const void* Q, const void* K, ea_dtype dtype, const int8_t* modes,
+                             const int32_t* cu_seqlens, int32_t B, int64_t total_tokens,
+                             int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             const ea_sparsity_params* params, const ea_xa_params* xa,
+                             float* xa_mass, uint8_t* xa_keep, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+ea_status ea_xa_prefill_run(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                            const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                            int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                            int32_t head_dim, const ea_sparsity_params* params,
+                            const ea_xa_params* xa, void* O, float* lse, const void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* ea_mfma_probe - measurement helper, not part of the attention path: the
  * practical bf16 matrix-core ceiling that the attention kernel's throughput is
  * set against beside the data-sheet peak (256 CUs x 2.4 GHz x 4096 FLOP/clk).

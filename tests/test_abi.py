@@ -22,7 +22,8 @@ def test_every_header_function_is_exported():
                           "ea_decode_workspace_size", "ea_decode_step",
                           "ea_hybrid_backward_workspace_size", "ea_hybrid_backward",
                           "ea_router_logit_grad_workspace_size", "ea_router_logit_grad",
-                          "ea_xa_prefill_workspace_size", "ea_xa_prefill"}
+                          "ea_xa_prefill_workspace_size", "ea_xa_prefill",
+                          "ea_xa_prefill_plan", "ea_xa_prefill_run"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -328,3 +329,14 @@ def test_xa_prefill_host_errors():
     assert call(ws_bytes=16) == -3
     # zero tokens launch nothing
     assert call(T=0, max_seqlen=0) == 0
+    # the two halves validate the same way
+    sp = bnd.SparsityParams(64, 1, 0, 0.2, 0.0)
+    xp = bnd.XAParams(128, 8, 0.9, 2)
+    assert L.ea_xa_prefill_plan(A, A, 0, A, A, 1, 1000, 1000, 8, 2, 128, ctypes.byref(sp),
+                                ctypes.byref(xp), None, None, A, 1 << 40, None) == -2
+    assert L.ea_xa_prefill_plan(None, A, 1, A, A, 1, 1000, 1000, 8, 2, 128, ctypes.byref(sp),
+                                ctypes.byref(xp), None, None, A, 1 << 40, None) == -1
+    assert L.ea_xa_prefill_run(A, A, A, 1, A, A, 1, 1000, 1000, 8, 2, 128, ctypes.byref(sp),
+                               None, A, None, A, 1 << 40, None) == -1
+    assert L.ea_xa_prefill_run(A, A, None, 1, A, A, 1, 1000, 1000, 8, 2, 128, ctypes.byref(sp),
+                               ctypes.byref(xp), A, None, A, 1 << 40, None) == -1

@@ -206,3 +206,24 @@ def test_xa_full_size_sampled():
     toks = np.array([i * 128 + o for i in rows for o in (0, 77, 127)])
     compare_rows(c, cmodes, O, lse, plan, matched, tokens=toks, heads=heads)
     assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(lse).all())
+
+
+def test_xa_plan_and_run_equal_the_one_shot_call():
+    c = gen.custom_case(91, [2500, 900], 8, 2, 128, "bf16", n_sink=1, keep_fraction=0.2,
+                        hitters=(0.1, 8.0))
+    dv = to_device(c)
+    modes = np.array([[0, 1], [1, 0]], np.int8)
+    note("xa plan + run vs one-shot")
+    O, lse, mass, keep = run_xa(c, modes, "XA-SSA", 0.9, dv)
+    m = torch.from_numpy(modes).cuda()
+    ws = torch.empty(ea.ea_xa_prefill_workspace_size(c.B, c.T, max_seqlen(c), c.Hq, c.Hkv, c.d, 1),
+                     dtype=torch.uint8, device="cuda")
+    ea.ea_xa_prefill_plan(dv["q"], dv["k"], m, dv["cu"], max_seqlen(c), ws, head_config="XA-SSA")
+    O2, lse2 = ea.ea_xa_prefill_run(dv["q"], dv["k"], dv["v"], m, dv["cu"], max_seqlen(c), ws,
+                                    head_config="XA-SSA")
+    # a second run over the same plan gives the same result
+    O3, lse3 = ea.ea_xa_prefill_run(dv["q"], dv["k"], dv["v"], m, dv["cu"], max_seqlen(c), ws,
+                                    head_config="XA-SSA")
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(lse, lse2)
+    assert torch.equal(O2, O3) and torch.equal(lse2, lse3)

@@ -34,3 +34,34 @@ def test_headline_effective_flops():
     m = np.array([[1, 1, 0, 1, 0, 1, 1, 1]])
     ef = metrics.effective_flops(m, [131072], 32, 8, 128, n_sink=1, keep_fraction=0.2)
     assert abs(ef - 7.324e13) / 7.324e13 < 1e-3
+
+
+def test_xa_effective_flops_matches_oracle_count():
+    # host bookkeeping of an XA layer vs the oracle's count over the same keep flags
+    from oracle import xa_oracle as xo
+    from full_attention_long_amd import metrics as mt
+    rng = np.random.default_rng(5)
+    lengths = np.array([1000, 300, 129])
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    Hq, Hkv, d = 8, 4, 64
+    modes = np.array([[1, 0, 1, 1], [0, 1, 1, 0], [1, 1, 1, 1]], np.int8)
+    for cfg in ("FA-XA", "XA-SSA", "FA-SSA"):
+        cm = mt.computation_modes(modes, cfg)
+        assert np.array_equal(cm, xo.computation_modes(modes, cfg))
+        nqb = -(-int(lengths.max()) // 128)
+        keep = np.zeros((3, Hq, nqb, nqb), np.uint8)
+        plan = {}
+        for b, L in enumerate(lengths):
+            nb = -(-int(L) // 128)
+            for hq in range(Hq):
+                if cm[b, hq // 2] != 2:
+                    continue
+                sel = np.tril(rng.random((nb, nb)) < 0.4)
+                sel[:, 0] = True
+                sel[np.arange(nb), np.arange(nb)] = True
+                sel = np.tril(sel)
+                keep[b, hq, :nb, :nb] = sel
+                plan[(b, hq)] = (None, sel)
+        got = mt.xa_effective_flops(cm, keep, lengths, Hq, Hkv, d, n_sink=1, keep_fraction=0.2)
+        want = xo.xa_effective_flops(cm, cu, Hq, Hkv, d, plan)
+        assert got == want, cfg
