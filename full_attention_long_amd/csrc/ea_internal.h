@@ -127,7 +127,9 @@ struct Workspace {
   // XA mode only (Shape.xa): per (sequence, KV head, query block) the number
   // of kept key blocks, and the triangular array of their list entries
   // (key block j | per-head mask << 16, ascending j)
-  size_t xa_cnt, xa_list, xa_rows;
+  // (and, per XA query head and query block, each group row's log2-sum-exp2
+  // over every key block: the selection's single-pass scratch)
+  size_t xa_cnt, xa_list, xa_rows, xa_lse;
   int32_t xa_nqb;      // query blocks of kXaBlock per sequence (upper bound)
 };
 

@@ -194,6 +194,7 @@ Workspace plan_workspace(const Shape& s) {
   w.xa_cnt = off;
   w.xa_list = off;
   w.xa_rows = off;
+  w.xa_lse = off;
   if (s.xa) {
     const int64_t rows = static_cast<int64_t>(s.B) * s.Hkv;
     off = align(off + sizeof(int32_t) * rows * w.xa_nqb);
@@ -201,6 +202,9 @@ Workspace plan_workspace(const Shape& s) {
     off = align(off + sizeof(int32_t) * rows * xa_row_offset(w.xa_nqb));
     w.xa_rows = off;
     off = align(off + sizeof(int32_t) * rows);
+    w.xa_lse = off;
+    off = align(off + sizeof(float) * kXaGroupsPerBlock * static_cast<int64_t>(s.B) * s.Hq *
+                          xa_row_offset(w.xa_nqb));
   }
   w.total = off;
   return w;

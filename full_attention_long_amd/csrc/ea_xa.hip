@@ -26,9 +26,11 @@
 // rows, the 8 rows of each group contiguous and groups padded by 16 bytes, so
 // that the 16 columns of a B operand read start on distinct bank groups and
 // every read is one base register plus an immediate offset), staged through
-// registers one block ahead.  The key blocks are walked twice: first for each group row's running
-// max and sum (online, per lane, merged over the 16 lanes of a row at the
-// end), then for the block masses, exp2(x - lse2) summed over the tile.
+// registers one block ahead.  The key blocks are walked once: per block, each
+// group row's log2-sum-exp2 over the block's 16 groups (DPP reductions over
+// the 16 lanes of the row) goes to the workspace and updates the row's running
+// total; once the totals are known, A[i][j] = sum over the rows of
+// 2^(block lse - row total).
 // The selection then runs in the same workgroup over its LDS row of masses: a
 // bitonic sort of the candidates (mass bits above the inverted block index,
 // so equal masses keep ascending index), a prefix sum in sorted order and the
@@ -62,6 +64,7 @@ struct XaArgs {
   const int32_t* meta;   // meta[kMetaXaRows]: number of XA rows
   const int32_t* rows;   // the XA (sequence, KV head) rows, b * Hkv + kvh
   int32_t* cnt;     // [B * Hkv * nqb]
+  float* lse;       // [B, Hq, xa_row_offset(nqb), 16] log2-sum-exp2 of each group row per key block
   int32_t* list;    // [B * Hkv * xa_row_offset(nqb)]
   float* mass;      // [B, Hq, nqb, nqb] or null
   uint8_t* keep;    // [B, Hq, nqb, nqb] or null
@@ -73,6 +76,29 @@ struct XaArgs {
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Max / sum over the 16 lanes of a DPP row, the result in every lane of it:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppSwap1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppSwap1>(v));
+  v = fmaxf(v, dpp<kDppSwap2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppMirror>(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -225,69 +251,76 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
                                    a.Q + (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + dim)
                              : bf16x8{};
     }
-    // lane holds group rows 16 i + 4 kq + e (e = 0..3) of the score tile
-    float lse2[4];
-    for (int pass = 0; pass < 2; ++pass) {
-      float m_e[4], l_e[4];
+    // Lane holds group rows 16 i + 4 kq + e (e = 0..3), key group 16 j + r,
+    // of each score tile.  Per key block: each row's log2-sum-exp2 over the
+    // block's 16 groups (a reduction over the 16 lanes of the row) goes to the
+    // workspace, and the row's running max and sum absorb it.
+    float M_e[4], L_e[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      M_e[e] = kMinusBig;
+      L_e[e] = 0.f;
+    }
+    float* const lrow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hq) * xa_row_offset(a.nqb) +
+                                 xa_row_offset(i)) * kXaGroupsPerBlock;
+    kfetch(0);
+    for (int j = 0; j <= i; ++j) {
+      __syncthreads();  // the previous tile (or sort keys) fully read
+      kstore();
+      __syncthreads();
+      if (j < i) kfetch(j + 1);
+      if (!hv) continue;
+      // B operand: key group column r (positions (16 j + r) S + t), same
+      // k-slice: group r, row t, dims 32 kk % D + 8 kq, i.e. element
+      // r KGS + 32 kk + 8 kq; four independent accumulation chains keep the
+      // matrix pipe busy
+      f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        sc[kk & 3] = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(Kt + r * KGS + 32 * kk + 8 * kq),
+                            sc[kk & 3]);
+      const f32x4 s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+      const int c = 16 * j + r;  // this lane's key group
+      f32x4 blse;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m_e[e] = kMinusBig;
-        l_e[e] = 0.f;
+        const int ag = 16 * i + 4 * kq + e;
+        const bool ok = c <= ag && ag < ng;
+        const float x = ok ? s[e] * a.cs : -INFINITY;
+        const float bm = row16_max(x);
+        const float ps = row16_sum(ok ? __builtin_amdgcn_exp2f(x - bm) : 0.f);
+        // an all-masked row of the block: bm = -inf, ps = 0, lse -inf, no change
+        blse[e] = bm + __log2f(ps);
+        const float mn = fmaxf(M_e[e], bm);
+        L_e[e] = L_e[e] * __builtin_amdgcn_exp2f(M_e[e] - mn) + ps * __builtin_amdgcn_exp2f(bm - mn);
+        M_e[e] = mn;
       }
-      kfetch(0);
-      for (int j = 0; j <= i; ++j) {
-        __syncthreads();  // the previous tile (or sort keys) fully read
-        kstore();
-        __syncthreads();
-        if (j < i) kfetch(j + 1);
-        if (!hv) continue;
-        // B operand: key group column r (positions (16 j + r) S + t), same
-        // k-slice: group r, row t, dims 32 kk % D + 8 kq, i.e. element
-        // r KGS + 32 kk + 8 kq; four independent accumulation chains keep the
-        // matrix pipe busy
-        f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+      if (r == 0) *reinterpret_cast<f32x4*>(lrow + j * kXaGroupsPerBlock + 4 * kq) = blse;
+    }
+    // Block masses A[i][j] = sum over the 16 rows of 2^(block lse - row lse),
+    // rows past the last group left out.  The row totals are uniform over
+    // the 16 lanes of a row; read them into scalars.
+    float rl[kXaGroupsPerBlock];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          sc[kk & 3] = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(Kt + r * KGS + 32 * kk + 8 * kq),
-                              sc[kk & 3]);
-        const f32x4 s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
-        const int c = 16 * j + r;  // this lane's key group
-        if (pass == 0) {
+    for (int e = 0; e < 4; ++e) {
+      const float tot = L_e[e] > 0.f ? M_e[e] + __log2f(L_e[e]) : INFINITY;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ag = 16 * i + 4 * kq + e;
-            const float x = (c <= ag && ag < ng) ? s[e] * a.cs : -INFINITY;
-            const float mn = fmaxf(m_e[e], x);
-            l_e[e] = l_e[e] * __builtin_amdgcn_exp2f(m_e[e] - mn) + __builtin_amdgcn_exp2f(x - mn);
-            m_e[e] = mn;
-          }
-        } else {
-          float ps = 0.f;
+      for (int q = 0; q < 4; ++q)
+        rl[4 * q + e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 16 * q));
+    }
+    __syncthreads();  // the workspace rows of every wave are written
+    if (hv) {
+      for (int j = lane; j <= i; j += 64) {
+        float m = 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ag = 16 * i + 4 * kq + e;
-            if (c <= ag && ag < ng) ps += __builtin_amdgcn_exp2f(s[e] * a.cs - lse2[e]);
-          }
-          ps = wave_sum(ps);
-          if (lane == 0) {
-            mass_l[wave * a.nqb + j] = ps;
-            if (a.mass)
-              a.mass[((static_cast<int64_t>(b) * a.Hq + hq) * a.nqb + i) * a.nqb + j] = ps;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(lrow + j * kXaGroupsPerBlock + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * i + 4 * q + e < ng) m += __builtin_amdgcn_exp2f(v[e] - rl[4 * q + e]);
         }
-      }
-      if (pass == 0) {
-        // merge the 16 lanes that share a group row
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float M = m_e[e];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-          float l = l_e[e] * __builtin_amdgcn_exp2f(m_e[e] - M);
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off, 64);
-          lse2[e] = M + __log2f(l);
-        }
+        mass_l[wave * a.nqb + j] = m;
+        if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hq) * a.nqb + i) * a.nqb + j] = m;
       }
     }
     __syncthreads();  // this quad's masses complete; the key tile is free
@@ -402,6 +435,7 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   a.rows = rows;
   a.cnt = reinterpret_cast<int32_t*>(base + ws.xa_cnt);
   a.list = reinterpret_cast<int32_t*>(base + ws.xa_list);
+  a.lse = reinterpret_cast<float*>(base + ws.xa_lse);
   a.mass = mass;
   a.keep = keep;
   a.B = s.B;

@@ -396,7 +396,10 @@ typedef struct {
 
 /* Bytes of device workspace ea_xa_prefill needs (0 if the sizes are invalid):
  * the routed prefill's work list plus, per (sequence, KV head, query block),
- * a count and the list of kept key blocks (a triangular array of int32). */
+ * a count and the list of kept key blocks (a triangular array of int32), and
+ * the selection's scratch: per (sequence, query head, query block i, key block
+ * j <= i) 16 float32 (about 64 * Hq * B * nqb^2 / 2 bytes: 1.07 GB at
+ * 128K tokens, Hq = 32). */
 size_t ea_xa_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max_seqlen,
                                     int32_t Hq, int32_t Hkv, int32_t head_dim, ea_dtype dtype);
 
@@ -414,12 +417,13 @@ size_t ea_xa_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t max
  * Rows of heads that are not XA, and rows past a sequence's last block, are
  * left untouched in xa_mass and xa_keep.  The selection is made per query
  * head; the attention kernel walks the union of a KV group's kept blocks and
- * masks each head to its own.  The masses are accumulated in float32 and the
- * threshold decision is taken in float32.  dtype must be EA_BF16; head_dim 64
+ * masks each head to its own.  Each key block is scored once: the
+ * log2-sum-exp2 of every group row over the block is kept in the workspace and
+ * turned into masses once the row's total is known.  The masses are
+ * accumulated in float32 and the threshold decision is taken in float32.  dtype must be EA_BF16; head_dim 64
  * or 128; Hq / Hkv <= 16 and a power of two >= 2 (a query tile then lies
  * inside one XA block); nqb <= 4096.  Work per XA query block grows with its
- * index (every earlier key block is scored twice: once for the group-row
- * softmax statistics, once for the masses). */
+ * index (every earlier key block is scored). */
 ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
                         const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
                         int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,

@@ -296,8 +296,10 @@ def test_xa_workspace_holds_the_selection_lists():
     one = ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
     xa = ea.ea_xa_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
     nqb = 131072 // 128
-    # counts [Hkv, nqb] and the triangular lists [Hkv, nqb (nqb + 1) / 2] of int32
-    need = 4 * 8 * nqb + 4 * 8 * nqb * (nqb + 1) // 2
+    tri = nqb * (nqb + 1) // 2
+    # counts [Hkv, nqb], the triangular lists [Hkv, tri] of int32, the XA rows
+    # [Hkv], and the selection's float32 scratch [Hq, tri, 16]
+    need = 4 * 8 * nqb + 4 * 8 * tri + 4 * 8 + 4 * 32 * tri * 16
     assert need <= xa - one <= need + 1024
     assert ea.ea_xa_prefill_workspace_size(1, 1000, 1000, 30, 8, 128, 1) == 0
 
