@@ -69,7 +69,6 @@ struct XaArgs {
   float* mass;      // [B, Hq, nqb, nqb] or null
   uint8_t* keep;    // [B, Hq, nqb, nqb] or null
   int32_t B, Hq, Hkv, G, nqb, nqb_pad, head_config;
-  int32_t region0;  // bytes of the K tile / sort region at the start of LDS
   float cs;         // softmax scale * log2(e) / S
   float tau;
 };
@@ -171,20 +170,26 @@ template <int D>
 __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
   constexpr int S = kXaStride;
   constexpr int KS = S * D / 32;                     // 32-wide k-steps of one group
-  constexpr int CPR = D / 8;                         // 16-byte chunks per key row
-  constexpr int NCH = kXaBlock * CPR / kXaThreads;   // chunks per thread per key tile
   constexpr int KGS = S * D + 8;                     // elements per padded key group
-  static_assert(NCH * kXaThreads == kXaBlock * CPR, "key tile must split evenly");
-  static_assert((kXaThreads / CPR) % S == 0, "a load round covers whole key groups");
+  constexpr int KT = kXaGroupsPerBlock * KGS;        // elements of one key tile
+  constexpr int RPI = 1024 / (2 * D);                // key rows per 1 KiB load instruction
+  constexpr int IPG = S / RPI;                       // load instructions per key group
+  constexpr int NDMA = kXaBlock / RPI / kXaWaves;    // load instructions per wave per tile
+  static_assert(IPG >= 1 && IPG * RPI == S, "a key group is whole load instructions");
+  static_assert(NDMA * RPI * kXaWaves == kXaBlock, "key tile must split evenly");
   static_assert(kXaGroupsPerBlock == 16, "one 16-row MFMA tile of groups per XA block");
 
+  // two key tiles, each addressed only through its own name, so that the
+  // direct loads into one can be in flight while the other is read; the
+  // first doubles as the sort buffer once the scoring is done
+  __shared__ __attribute__((aligned(1024))) uint16_t Kt0[KT], Kt1[KT];
+  __shared__ float rlt[kXaWaves][kXaGroupsPerBlock];  // group-row totals of the quad's heads
+  __shared__ float fz[2];                              // masses of the forced blocks
+  __shared__ float redf[kXaWaves + 1];
+  __shared__ int32_t redi[kXaWaves + 1];
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);            // key tile, then sort keys
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
-  float* mass_l = reinterpret_cast<float*>(smem + a.region0);  // [kXaWaves][nqb]
-  uint32_t* hm = reinterpret_cast<uint32_t*>(mass_l + kXaWaves * a.nqb);  // [nqb]
-  float* redf = reinterpret_cast<float*>(hm + a.nqb);          // [kXaWaves + 1]
-  int32_t* redi = reinterpret_cast<int32_t*>(redf + kXaWaves + 1);
+  uint32_t* hm = reinterpret_cast<uint32_t*>(smem);    // [nqb] heads keeping block j
+  uint64_t* keys = reinterpret_cast<uint64_t*>(Kt0);
 
   // Work item t = the workgroup's position in the XCD-chunked order
   // (list_position): items run in bands of kXcdChunk query blocks, the
@@ -208,32 +213,35 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
   const int r = lane % 16, kq = lane / 16;
   for (int j = tid; j <= i; j += kXaThreads) hm[j] = 0u;
 
-  // Key rows of block j through a buffer resource that ends at the sequence
-  // end (rows past it read as zeros; the whole offset is in the range-checked
-  // vector offset): thread tid loads chunk tid % CPR of rows
-  // tid / CPR + n (kXaThreads / CPR), n < NCH.
-  constexpr int RPN = kXaThreads / CPR;  // rows per load round
-  const int rs2 = a.Hkv * D * 2;         // bytes between key rows
-  const int koff = (tid / CPR) * rs2 + (tid % CPR) * 16;
+  // Direct loads of key block j: instruction q = wave NDMA + n of the tile
+  // fills rows (q % IPG) RPI .. + RPI - 1 of group q / IPG, lane l writing
+  // 16-byte chunk l % (D / 8) of row l / (D / 8).  The buffer resource ends at
+  // the sequence end (rows past it read as zeros; the whole offset is in the
+  // range-checked vector offset).  LDS: the 8 rows of a group contiguous,
+  // groups padded by 16 bytes, so the 16 groups a B-operand read touches start
+  // on 16 distinct 16-byte bank groups.
+  const int rs2 = a.Hkv * D * 2;  // bytes between key rows
   const uint16_t* kseq = a.K + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
-  u32x4 kreg[NCH];
-  auto kfetch = [&](int j) {
+  int dma_off[NDMA];
+#pragma unroll
+  for (int n = 0; n < NDMA; ++n) {
+    const int q = wave * NDMA + n;
+    dma_off[n] = ((q / IPG) * S + (q % IPG) * RPI + lane / (D / 8)) * rs2 + (lane % (D / 8)) * 16;
+  }
+  // (the offsets come in as a parameter: a lambda capturing a local array
+  // by reference makes the host pass drop this kernel's launch stub)
+  auto dma = [&](uint16_t* tile, int j, const int* off) {
     const int key0 = j * kXaBlock;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kseq + static_cast<int64_t>(key0) * a.Hkv * D), 0,
         static_cast<unsigned>(L - key0) * static_cast<unsigned>(rs2), kBufferWord3);
 #pragma unroll
-    for (int n = 0; n < NCH; ++n)
-      kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, koff + n * RPN * rs2, 0, 0));
-  };
-  // LDS: the 8 rows of one key group are contiguous, groups padded by 16
-  // bytes, so the 16 groups a B operand read touches start on 16 distinct
-  // 16-byte bank groups
-  const int kst = (tid / CPR / S) * KGS + ((tid / CPR) % S) * D + (tid % CPR) * 8;
-  auto kstore = [&]() {
-#pragma unroll
-    for (int n = 0; n < NCH; ++n)
-      *reinterpret_cast<u32x4*>(Kt + kst + n * (RPN / S) * KGS) = kreg[n];
+    for (int n = 0; n < NDMA; ++n) {
+      const int q = wave * NDMA + n;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(tile + (q / IPG) * KGS + (q % IPG) * RPI * D),
+          16, off[n], 0, 0, 0);
+    }
   };
 
   for (int g0 = 0; g0 < a.G; g0 += kXaWaves) {
@@ -263,88 +271,88 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
     }
     float* const lrow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hq) * xa_row_offset(a.nqb) +
                                  xa_row_offset(i)) * kXaGroupsPerBlock;
-    kfetch(0);
-    for (int j = 0; j <= i; ++j) {
-      __syncthreads();  // the previous tile (or sort keys) fully read
-      kstore();
-      __syncthreads();
-      if (j < i) kfetch(j + 1);
-      if (!hv) continue;
-      // B operand: key group column r (positions (16 j + r) S + t), same
-      // k-slice: group r, row t, dims 32 kk % D + 8 kq, i.e. element
-      // r KGS + 32 kk + 8 kq; four independent accumulation chains keep the
-      // matrix pipe busy
-      f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    // block j from tile kt while block j + 1 loads into knext; the barrier at
+    // the end waits for that load and for every wave's reads of kt
+    auto step = [&](int j, const uint16_t* kt, uint16_t* knext) {
+      if (j < i) dma(knext, j + 1, dma_off);
+      if (hv) {
+        // B operand: key group column r (positions (16 j + r) S + t), same
+        // k-slice: group r, row t, dims 32 kk % D + 8 kq, i.e. element
+        // r KGS + 32 kk + 8 kq; four independent accumulation chains keep
+        // the matrix pipe busy
+        f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        sc[kk & 3] = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(Kt + r * KGS + 32 * kk + 8 * kq),
-                            sc[kk & 3]);
-      const f32x4 s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
-      const int c = 16 * j + r;  // this lane's key group
-      f32x4 blse;
+        for (int kk = 0; kk < KS; ++kk)
+          sc[kk & 3] = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(kt + r * KGS + 32 * kk + 8 * kq),
+                              sc[kk & 3]);
+        const f32x4 s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+        const int c = 16 * j + r;  // this lane's key group
+        f32x4 blse;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ag = 16 * i + 4 * kq + e;
-        const bool ok = c <= ag && ag < ng;
-        const float x = ok ? s[e] * a.cs : -INFINITY;
-        const float bm = row16_max(x);
-        const float ps = row16_sum(ok ? __builtin_amdgcn_exp2f(x - bm) : 0.f);
-        // an all-masked row of the block: bm = -inf, ps = 0, lse -inf, no change
-        blse[e] = bm + __log2f(ps);
-        const float mn = fmaxf(M_e[e], bm);
-        L_e[e] = L_e[e] * __builtin_amdgcn_exp2f(M_e[e] - mn) + ps * __builtin_amdgcn_exp2f(bm - mn);
-        M_e[e] = mn;
-      }
-      if (r == 0) *reinterpret_cast<f32x4*>(lrow + j * kXaGroupsPerBlock + 4 * kq) = blse;
-    }
-    // Block masses A[i][j] = sum over the 16 rows of 2^(block lse - row lse),
-    // rows past the last group left out.  The row totals are uniform over
-    // the 16 lanes of a row; read them into scalars.
-    float rl[kXaGroupsPerBlock];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float tot = L_e[e] > 0.f ? M_e[e] + __log2f(L_e[e]) : INFINITY;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        rl[4 * q + e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 16 * q));
-    }
-    __syncthreads();  // the workspace rows of every wave are written
-    if (hv) {
-      for (int j = lane; j <= i; j += 64) {
-        float m = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(lrow + j * kXaGroupsPerBlock + 4 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (16 * i + 4 * q + e < ng) m += __builtin_amdgcn_exp2f(v[e] - rl[4 * q + e]);
+        for (int e = 0; e < 4; ++e) {
+          const int ag = 16 * i + 4 * kq + e;
+          const bool ok = c <= ag && ag < ng;
+          const float x = ok ? s[e] * a.cs : -INFINITY;
+          const float bm = row16_max(x);
+          const float ps = row16_sum(ok ? __builtin_amdgcn_exp2f(x - bm) : 0.f);
+          // an all-masked row of the block: bm = -inf, ps = 0, lse -inf, no change
+          blse[e] = bm + __log2f(ps);
+          const float mn = fmaxf(M_e[e], bm);
+          L_e[e] = L_e[e] * __builtin_amdgcn_exp2f(M_e[e] - mn) + ps * __builtin_amdgcn_exp2f(bm - mn);
+          M_e[e] = mn;
         }
-        mass_l[wave * a.nqb + j] = m;
-        if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hq) * a.nqb + i) * a.nqb + j] = m;
+        if (r == 0) *reinterpret_cast<f32x4*>(lrow + j * kXaGroupsPerBlock + 4 * kq) = blse;
       }
+      __syncthreads();
+    };
+    dma(Kt0, 0, dma_off);
+    __syncthreads();
+    for (int j = 0; j <= i; j += 2) {
+      step(j, Kt0, Kt1);
+      if (j + 1 <= i) step(j + 1, Kt1, Kt0);
     }
-    __syncthreads();  // this quad's masses complete; the key tile is free
+    // the quad's group-row totals (uniform over the 16 lanes of a row)
+    if (hv && r == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rlt[wave][4 * kq + e] = M_e[e] + __log2f(L_e[e]);
+    }
+    __syncthreads();  // totals and workspace rows written; the key tiles are free
 
-    // Threshold selection of each head of the quad, the whole workgroup at a time.
+    // Threshold selection of each head of the quad, the whole workgroup at a
+    // time.  Block masses A[i][j] = sum over the group rows (those before the
+    // sequence's last group) of 2^(block lse - row total).
     for (int w = 0; w < kXaWaves && g0 + w < a.G; ++w) {
-      const float* mrow = mass_l + w * a.nqb;
+      const int hqw = kvh * a.G + g0 + w;
+      const float* srow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hqw) * xa_row_offset(a.nqb) +
+                                   xa_row_offset(i)) * kXaGroupsPerBlock;
       const uint32_t bit = 1u << (g0 + w);
-      float part = 0.f;
-      for (int j = tid; j <= i; j += kXaThreads) part += mrow[j];
-      const float total = block_sum(part, redf);
-      const float target = a.tau * total;
-      const float forced = i > 0 ? mrow[0] + mrow[i] : mrow[0];
       const int m = i - 1;  // candidates: blocks 1 .. i-1
       int P2 = 1;
       while (P2 < m) P2 <<= 1;
-      if (m > 0) {
-        for (int p = tid; p < P2; p += kXaThreads) {
-          const int j = p + 1;
-          keys[p] = p < m ? (static_cast<uint64_t>(__float_as_uint(mrow[j])) << 32) |
-                                static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(j))
-                          : 0ull;
+      float part = 0.f;
+      for (int j = tid; j <= i; j += kXaThreads) {
+        float mj = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(srow + j * kXaGroupsPerBlock + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * i + 4 * q + e < ng) mj += __builtin_amdgcn_exp2f(v[e] - rlt[w][4 * q + e]);
         }
-        __syncthreads();
+        part += mj;
+        if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + i) * a.nqb + j] = mj;
+        if (j == 0) fz[0] = mj;
+        if (j == i) fz[1] = mj;
+        if (j >= 1 && j < i)
+          keys[j - 1] = (static_cast<uint64_t>(__float_as_uint(mj)) << 32) |
+                        static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(j));
+      }
+      for (int p = m + tid; p < P2; p += kXaThreads)
+        if (p >= 0) keys[p] = 0ull;
+      const float total = block_sum(part, redf);  // its barriers publish keys and fz
+      const float target = a.tau * total;
+      const float forced = i > 0 ? fz[0] + fz[1] : fz[0];
+      if (m > 0) {
         // bitonic sort, descending
         for (int k = 2; k <= P2; k <<= 1) {
           for (int jj = k >> 1; jj > 0; jj >>= 1) {
@@ -385,14 +393,14 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
       }
       __syncthreads();
       if (a.keep) {
-        uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + kvh * a.G + g0 + w) * a.nqb + i) * a.nqb;
+        uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + i) * a.nqb;
         for (int j = tid; j <= i; j += kXaThreads) krow[j] = (hm[j] & bit) ? 1 : 0;
       }
     }
+    __syncthreads();  // the sort buffer (first key tile) is free again
   }
 
   // Ascending list of the key blocks some head of the group keeps.
-  __syncthreads();
   const int per = (i + 1 + kXaThreads - 1) / kXaThreads;
   const int j0 = tid * per;
   int32_t mine = 0;
@@ -410,14 +418,12 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
 
 size_t xa_plan_lds_bytes(const Shape& s) {
   const int nqb = (s.max_seqlen + kXaBlock - 1) / kXaBlock;
-  if (nqb > 4096) return 0;
   int P2 = 1;
   while (P2 < nqb) P2 <<= 1;
+  // the sort keys of one query block reuse the first key tile
   const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + 8) * 2;
-  const size_t region0 = ktile > 8u * P2 ? ktile : 8u * P2;
-  const size_t bytes = region0 + sizeof(float) * kXaWaves * nqb + sizeof(uint32_t) * nqb +
-                       sizeof(float) * (2 * kXaWaves + 2);
-  return bytes <= 160u * 1024u ? bytes : 0;
+  if (nqb > 4096 || 8u * static_cast<size_t>(P2) > ktile) return 0;
+  return sizeof(uint32_t) * static_cast<size_t>(nqb);
 }
 
 hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const void* Q,
@@ -445,10 +451,6 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   a.nqb = ws.xa_nqb;
   a.nqb_pad = (ws.xa_nqb + kXcdChunk - 1) / kXcdChunk * kXcdChunk;
   a.head_config = s.head_config;
-  int P2 = 1;
-  while (P2 < a.nqb) P2 <<= 1;
-  const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + 8) * 2;
-  a.region0 = static_cast<int32_t>(ktile > 8u * P2 ? ktile : 8u * P2);
   a.cs = g.scale * kLog2e / kXaStride;
   a.tau = tau;
   const size_t lds = xa_plan_lds_bytes(s);
