@@ -127,13 +127,13 @@ def xa_effective_flops(cmodes, keep, lengths, Hq: int, Hkv: int, d: int, *, n_si
 
 def xa_selection_flops(cmodes, lengths, Hq: int, Hkv: int, d: int, stride: int = 8) -> int:
     """Matrix FLOPs of the XA selection: per XA query head and query block i,
-    i + 1 key blocks of 16 x 16 group scores over S * d products, scored
-    twice (statistics pass and mass pass)."""
+    i + 1 key blocks of 16 x 16 group scores over S * d products, each
+    scored once."""
     G = Hq // Hkv
     per_tile = 2 * (XA_BLOCK // stride) ** 2 * stride * d
     total = 0
     for b, L in enumerate(lengths):
         nb = -(-int(L) // XA_BLOCK)
         n_xa = int((np.asarray(cmodes[b]) == 2).sum()) * G
-        total += n_xa * 2 * per_tile * (nb * (nb + 1) // 2)
+        total += n_xa * per_tile * (nb * (nb + 1) // 2)
     return total
