@@ -65,3 +65,14 @@ def test_xa_effective_flops_matches_oracle_count():
         got = mt.xa_effective_flops(cm, keep, lengths, Hq, Hkv, d, n_sink=1, keep_fraction=0.2)
         want = xo.xa_effective_flops(cm, cu, Hq, Hkv, d, plan)
         assert got == want, cfg
+
+
+def test_xa_selection_flops_closed_form():
+    # one scoring of every causal 16 x 16 group tile (S = 8, d = 128):
+    # 2 * 16 * 16 * 8 * 128 FLOP per tile, nb (nb + 1) / 2 tiles per XA query head
+    from full_attention_long_amd import metrics as mt
+    cm = np.array([[2, 1], [0, 2]])
+    lengths = np.array([1024, 300])
+    got = mt.xa_selection_flops(cm, lengths, 8, 2, 128)
+    tile = 2 * 16 * 16 * 8 * 128
+    assert got == 4 * tile * (8 * 9 // 2) + 4 * tile * (3 * 4 // 2)
