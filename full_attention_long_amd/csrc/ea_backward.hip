@@ -15,9 +15,10 @@
 // Three kernels: bwd_pre_kernel (D and LSE in log2 units per row),
 // bwd_dq_kernel (query-tile stationary, the forward's work list and K/V
 // tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with 32x32x16 MFMAs)
-// and bwd_dkv_kernel (key stationary: each wave owns 16 keys of its KV head
-// and walks the query blocks that can see them, head by head: S = Q K^T,
-// dP = dO V^T, dV += P^T dO, dK += dS^T Q with 16x16x32 MFMAs).
+// and bwd_dkv_kernel (key stationary, launched once per output: each wave
+// owns 32 keys of its KV head and walks the query blocks that can see them,
+// head by head: S = Q K^T and dV += P^T dO, or S, dP = dO V^T and
+// dK += dS^T Q, with 16x16x32 MFMAs).
 #include "ea_internal.h"
 
 #include <math.h>
@@ -194,14 +195,23 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   auto block = [&](int kb, const uint16_t* kr_, const uint16_t* vr_, const uint16_t* kt_) {
     f32x16 s0, s1, p0v, p1v;
     rowmm(kr_, qf, s0, s1);
-    const bool full = block_full(mode, kb, p0, qb0, qb1, ns, w);
-    const bool blk_ok = block_visible(mode, kb, qblk, ns, w);
+    // a block every row of the tile sees (the common case) skips the
+    // per-element visibility test
+    if (block_full(mode, kb, p0, qb0, qb1, ns, w)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
-      const bool v0 = full || (blk_ok && j <= pos), v1 = full || (blk_ok && j + 32 <= pos);
-      s0[i] = v0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -lrow)) : 0.f;
-      s1[i] = v1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lrow)) : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -lrow));
+        s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lrow));
+      }
+    } else {
+      const bool blk_ok = block_visible(mode, kb, qblk, ns, w);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb * kBlock + 8 * (i / 4) + 4 * h + (i % 4);
+        const bool v0 = blk_ok && j <= pos, v1 = blk_ok && j + 32 <= pos;
+        s0[i] = v0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -lrow)) : 0.f;
+        s1[i] = v1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lrow)) : 0.f;
+      }
     }
     rowmm(vr_, of, p0v, p1v);  // dP^T
     bf16x8 dsb[4];
@@ -262,14 +272,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: a workgroup owns kDkvKeys keys of one KV head of one sequence, 16
-// per wave, and walks the query blocks that can see them; for
-// each query block and each of the G query heads it stages that head's Q and
-// dO rows, LSE and D in LDS (the next stage prefetched into registers).
+// dK, dV: a workgroup owns kDkvKeys keys of one KV head of one sequence, 32
+// per wave as two 16-key tiles, and walks the query blocks that can see them;
+// for each query block and each of the G query heads it stages that head's Q
+// and dO rows, LSE and D in LDS (the next stage prefetched into registers).
+// Two launches split the work by role: ROLE 0 rebuilds P and accumulates
+// dV += P^T dO, ROLE 1 rebuilds P and dP and accumulates dK += dS^T Q.  Each
+// Q / dO operand read from LDS feeds the MFMAs of both key tiles, so a role
+// reads half the LDS bytes per product that one wave owning 16 keys of both
+// outputs did; the price is S computed by both roles (five products per key
+// and query instead of four), and each role fits two waves per SIMD.
 // ---------------------------------------------------------------------------
 constexpr int kDkvThreads = 64 * kDkvWaves;
+constexpr int kDkvKeysPerWave = kDkvKeys / kDkvWaves;
+static_assert(kDkvKeysPerWave == 32, "two 16-key tiles per wave");
 
-template <int D>
+template <int D, int ROLE>
 __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int NU = D / 32;    // 32-wide d steps
   constexpr int NM = D / 16;    // 16-wide d tiles of dK, dV
@@ -298,120 +316,181 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, lg = lane / 16, li = lane % 16;
-  const int key_b = pair * kDkvKeys + wave * 16 + li;  // this lane's key as a B column
-  const int kbj = key_b / kBlock;
-  // K and V rows as the B operands of S = Q K^T and dP = dO V^T
-  bf16x8 kf[NU], vf[NU];
-  {
-    const bool kv = key_b < L;
-    const int64_t r = (static_cast<int64_t>(tok0 + (kv ? key_b : 0)) * a.Hkv + g) * D;
+  // this lane's key of key tile c as a B column, and its block
+  int key_b[2], kbj[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    key_b[c] = pair * kDkvKeys + wave * kDkvKeysPerWave + 16 * c + li;
+    kbj[c] = key_b[c] / kBlock;
+  }
+  // K (both roles) and V (ROLE 1) rows as the B operands of S = Q K^T and
+  // dP = dO V^T
+  bf16x8 kf[2][NU], vf[2][NU];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const bool kv = key_b[c] < L;
+    const int64_t r = (static_cast<int64_t>(tok0 + (kv ? key_b[c] : 0)) * a.Hkv + g) * D;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      kf[u] = kv ? *reinterpret_cast<const bf16x8*>(a.K + r + 32 * u + 8 * lg) : bf16x8{};
-      vf[u] = kv ? *reinterpret_cast<const bf16x8*>(a.V + r + 32 * u + 8 * lg) : bf16x8{};
+      kf[c][u] = kv ? *reinterpret_cast<const bf16x8*>(a.K + r + 32 * u + 8 * lg) : bf16x8{};
+      if constexpr (ROLE == 1)
+        vf[c][u] = kv ? *reinterpret_cast<const bf16x8*>(a.V + r + 32 * u + 8 * lg) : bf16x8{};
     }
   }
-  f32x4 dk[NM], dv[NM];
+  f32x4 acc[2][NM];  // dV (ROLE 0) or dK (ROLE 1)
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    dk[m] = f32x4{};
-    dv[m] = f32x4{};
-  }
-  const float c = a.scale * kLog2e;
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[c][m] = f32x4{};
+  const float cl = a.scale * kLog2e;
 
-  // stage (qb, hh) -> registers
-  u32x4 qreg[NCH], oreg[NCH];
-  float lreg = 0.f, dreg = 0.f;
-  auto fetch = [&](int qb, int hh) {
-    const int hq = g * a.G + hh;
+  // stage (qb, hh) -> registers, two stages ahead (set x holds the stages
+  // of parity x), so a stage's loads have two steps of work to land in
+  u32x4 qreg[2][NCH], oreg[2][NCH];
+  float lreg[2] = {0.f, 0.f}, dreg[2] = {0.f, 0.f};
+  auto fetch = [&](int x, int st) {
+    const int qb = qb_lo + st / a.G;
+    const int hq = g * a.G + st % a.G;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
       const int p = qb * kBlock + r;
       const int64_t src = (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + col;
-      qreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
-      oreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.dO + src) : u32x4{0, 0, 0, 0};
+      qreg[x][k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
+      oreg[x][k] = p < L ? *reinterpret_cast<const u32x4*>(a.dO + src) : u32x4{0, 0, 0, 0};
     }
     if (tid < kBlock) {
       const int p = qb * kBlock + tid;
       const int64_t ix = static_cast<int64_t>(hq) * a.T + tok0 + p;
-      lreg = p < L ? a.lse2[ix] : INFINITY;
-      dreg = p < L ? a.Dv[ix] : 0.f;
+      lreg[x] = p < L ? a.lse2[ix] : INFINITY;
+      if constexpr (ROLE == 1) dreg[x] = p < L ? a.Dv[ix] : 0.f;
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int x) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Qs + r * QROW + col) = qreg[k];
-      *reinterpret_cast<u32x4*>(Os + r * QROW + col) = oreg[k];
+      *reinterpret_cast<u32x4*>(Qs + r * QROW + col) = qreg[x][k];
+      *reinterpret_cast<u32x4*>(Os + r * QROW + col) = oreg[x][k];
     }
     if (tid < kBlock) {
-      Ls[tid] = lreg;
-      Ds[tid] = dreg;
+      Ls[tid] = lreg[x];
+      Ds[tid] = dreg[x];
     }
   };
 
   const int nsteps = (qb_hi - qb_lo + 1) * a.G;
-  fetch(qb_lo, 0);
-  for (int st = 0; st < nsteps; ++st) {
+  fetch(0, 0);
+  if (nsteps > 1) fetch(1, 1);
+  // one step of the walk; x = st & 1, written out per parity so that the
+  // register sets are named statically
+  auto step = [&](int st, int x) {
     const int qb = qb_lo + st / a.G;
     __syncthreads();  // the previous step's reads of the tiles are done
-    stage();
+    stage(x);
     __syncthreads();
-    if (st + 1 < nsteps) fetch(qb_lo + (st + 1) / a.G, (st + 1) % a.G);
+    if (st + 2 < nsteps) fetch(x, st + 2);
 
-    // S and dP: 4 query tiles of 16 rows; lane holds key li, rows 16 qt + 4 lg + i
-    f32x4 s[4], dp[4];
+    // whether every row of query block qb sees every key of key tile c (the
+    // tile's 16 keys share one 64-key block; wave-uniform)
+    bool full[2];
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      s[qt] = f32x4{};
-      dp[qt] = f32x4{};
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int off = (16 * qt + li) * QROW + 32 * u + 8 * lg;
-        s[qt] = mfma16(*reinterpret_cast<const bf16x8*>(Qs + off), kf[u], s[qt]);
-        dp[qt] = mfma16(*reinterpret_cast<const bf16x8*>(Os + off), vf[u], dp[qt]);
-      }
+    for (int c = 0; c < 2; ++c) {
+      const int klast = pair * kDkvKeys + wave * kDkvKeysPerWave + 16 * c + 15;
+      full[c] = klast <= qb * kBlock && qb * kBlock + kBlock <= L &&
+                (mode == kModeFA || kbj[c] < ns || qb - kbj[c] < w);
     }
-    // P and dS (as bf16 A operands: keys x 32 queries per pair of tiles)
-    bf16x8 pa[2], da[2];
+    // Two halves of 32 query rows; per half, S (and dP) as 2 query tiles of
+    // 16 rows x 2 key tiles: lane holds key li of tile c, rows 16 qt + 4 lg + i
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * qt + 4 * lg);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * qt + 4 * lg);
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 s[2][2], dp[2][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = qb * kBlock + 16 * qt + 4 * lg + i;
-        const bool vis = key_b <= p && p < L &&
-                         (mode == kModeFA || kbj < ns || p / kBlock - kbj < w);
-        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][i], c, -lv[i])) : 0.f;
-        pa[qt / 2][4 * (qt & 1) + i] = static_cast<__bf16>(pv);
-        da[qt / 2][4 * (qt & 1) + i] = static_cast<__bf16>(pv * (dp[qt][i] - dv4[i]));
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int qt = 2 * hf + t2;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          s[t2][c] = f32x4{};
+          dp[t2][c] = f32x4{};
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int off = (16 * qt + li) * QROW + 32 * u + 8 * lg;
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + off);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) s[t2][c] = mfma16(qa, kf[c][u], s[t2][c]);
+          if constexpr (ROLE == 1) {
+            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Os + off);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) dp[t2][c] = mfma16(oa, vf[c][u], dp[t2][c]);
+          }
+        }
       }
-    }
-    // dV += P^T dO, dK += dS^T Q: B from the tiles by transposing reads, query
-    // rows 32 p2 + 4 lg + 0..3 and + 16, the order pa / da hold them in
+      // P (ROLE 0) or dS (ROLE 1) as bf16 A operands: keys x the half's 32
+      // queries, in the order the transposed B reads deliver them.  A key
+      // tile that every row of the query block sees (below the diagonal,
+      // inside the window, rows before the sequence end: the common case)
+      // skips the per-element visibility test.
+      bf16x8 pa[2];
 #pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2)
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int qt = 2 * hf + t2;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * qt + 4 * lg);
+        f32x4 dv4 = f32x4{};
+        if constexpr (ROLE == 1) dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * qt + 4 * lg);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x4 pv;
+          if (full[c]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][c][i], cl, -lv[i]));
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int p = qb * kBlock + 16 * qt + 4 * lg + i;
+              const bool vis = key_b[c] <= p && p < L &&
+                               (mode == kModeFA || kbj[c] < ns || p / kBlock - kbj[c] < w);
+              pv[i] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][c][i], cl, -lv[i])) : 0.f;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (ROLE == 0) pa[c][4 * t2 + i] = static_cast<__bf16>(pv[i]);
+            else pa[c][4 * t2 + i] = static_cast<__bf16>(pv[i] * (dp[t2][c][i] - dv4[i]));
+          }
+        }
+      }
+      // dV += P^T dO (ROLE 0) or dK += dS^T Q (ROLE 1): B from the tiles by
+      // transposing reads, query rows 32 hf + 4 lg + 0..3 and + 16, the order
+      // pa holds them in; each read feeds both key tiles
+      const uint16_t* src = ROLE == 0 ? Os : Qs;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const int off = (32 * p2 + 4 * lg + li / 4) * QROW + 16 * m + 4 * (li & 3);
-        dv[m] = mfma16(pa[p2], tr_pair(Os + off, Os + off + 16 * QROW), dv[m]);
-        dk[m] = mfma16(da[p2], tr_pair(Qs + off, Qs + off + 16 * QROW), dk[m]);
+        const int off = (32 * hf + 4 * lg + li / 4) * QROW + 16 * m + 4 * (li & 3);
+        const bf16x8 bt = tr_pair(src + off, src + off + 16 * QROW);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[c][m] = mfma16(pa[c], bt, acc[c][m]);
       }
+    }
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, 0);
+    if (st + 1 < nsteps) step(st + 1, 1);
   }
 
-  // lane holds keys wave 16 + 4 lg + i, dims 16 m + li
+  // lane holds keys 16 c + 4 lg + i of the wave's 32, dims 16 m + li
+  uint16_t* const out = ROLE == 0 ? a.dV : a.dK;
+  const float osc = ROLE == 0 ? 1.f : a.scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = pair * kDkvKeys + wave * 16 + 4 * lg + i;
-    if (key >= L) continue;
-    const int64_t r = (static_cast<int64_t>(tok0 + key) * a.Hkv + g) * D;
+  for (int c = 0; c < 2; ++c) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      a.dK[r + 16 * m + li] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dk[m][i] * a.scale));
-      a.dV[r + 16 * m + li] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dv[m][i]));
+    for (int i = 0; i < 4; ++i) {
+      const int key = pair * kDkvKeys + wave * kDkvKeysPerWave + 16 * c + 4 * lg + i;
+      if (key >= L) continue;
+      const int64_t r = (static_cast<int64_t>(tok0 + key) * a.Hkv + g) * D;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        out[r + 16 * m + li] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[c][m][i] * osc));
     }
   }
 }
@@ -499,12 +578,15 @@ hipError_t launch_backward(const Shape& s, const Geometry& g, BwdArgs args, cons
   if (e != hipSuccess) return e;
   constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
   const unsigned grid = static_cast<unsigned>((args.max_items + span - 1) / span * span);
+  const dim3 dkv_grid(static_cast<unsigned>(dkv_items));
   if (s.d == 128) {
     hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<128>), dim3(static_cast<unsigned>(dkv_items)), dim3(kDkvThreads), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128, 0>), dkv_grid, dim3(kDkvThreads), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128, 1>), dkv_grid, dim3(kDkvThreads), 0, st, args);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<64>), dim3(static_cast<unsigned>(dkv_items)), dim3(kDkvThreads), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64, 0>), dkv_grid, dim3(kDkvThreads), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64, 1>), dkv_grid, dim3(kDkvThreads), 0, st, args);
   }
   return hipGetLastError();
 }
