@@ -504,6 +504,8 @@ ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes,
     return fail(EA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   ea::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
   a.O = static_cast<uint16_t*>(O);
   a.lse = lse;
   a.Hq = Hq;
@@ -515,8 +517,7 @@ ea_status ea_decode_step(const ea_kvcache_desc* desc, void* cache, size_t bytes,
   a.o_part = static_cast<float*>(workspace);
   a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         ((rows * desc->head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)));
-  hipError_t e = ea::launch_decode(cache_view(desc, cache, bytes), a, k_new, v_new,
-                                   static_cast<hipStream_t>(stream));
+  hipError_t e = ea::launch_decode(cache_view(desc, cache, bytes), a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(EA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -140,23 +140,6 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(CacheView c, const int3
     for (int b = threadIdx.x; b < c.B; b += blockDim.x) c.lengths[b] = cu[b + 1] - cu[b];
 }
 
-// The new token's K and V rows at position lengths[b].
-__global__ __launch_bounds__(256) void cache_append_kernel(CacheView c, const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v) {
-  const int cpr = c.d / 8;
-  const int64_t total = static_cast<int64_t>(c.B) * c.Hkv * cpr;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int64_t slot = i / cpr;
-  const int ch = static_cast<int>(i - slot * cpr);
-  const int b = static_cast<int>(slot / c.Hkv);
-  const int p = c.lengths[b];
-  if (p >= c.max_len || !c.valid[0]) return;  // full or unusable: precondition violated
-  const int64_t dst = block_offset(c, phys_block(c, slot, p / kBlock)) + (p % kBlock) * c.d + ch * 8;
-  *reinterpret_cast<u32x4*>(c.K + dst) = *reinterpret_cast<const u32x4*>(k + slot * c.d + ch * 8);
-  *reinterpret_cast<u32x4*>(c.V + dst) = *reinterpret_cast<const u32x4*>(v + slot * c.d + ch * 8);
-}
-
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -194,6 +177,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attn_kernel(CacheView c
   const KeyRange kr = key_range(mode, qb, qb, c.n_sink, w);
   const int n_vis = full ? 0 : kr.count();
   const int v0 = chunk * a.chunk_blocks, v1 = min(n_vis, v0 + a.chunk_blocks);
+
+  // The new token's K and V rows go to position pos of the slot, written by
+  // the workgroup whose chunk holds that block (the last visible one), before
+  // its waves read the block.
+  if (!full && chunk == (n_vis - 1) / a.chunk_blocks) {
+    const int64_t dst = block_offset(c, phys_block(c, slot, qb)) + (pos % kBlock) * D;
+    for (int ch = threadIdx.x; ch < D / 8; ch += kDecodeThreads) {
+      *reinterpret_cast<u32x4*>(c.K + dst + ch * 8) = *reinterpret_cast<const u32x4*>(a.k_new + slot * D + ch * 8);
+      *reinterpret_cast<u32x4*>(c.V + dst + ch * 8) = *reinterpret_cast<const u32x4*>(a.v_new + slot * D + ch * 8);
+    }
+    __syncthreads();
+  }
+
   if (v0 >= v1) {  // nothing visible in this chunk
     if (threadIdx.x < a.G) a.lse_part[(part0 + static_cast<int64_t>(threadIdx.x) * a.n_chunks) + chunk] = -INFINITY;
     return;
@@ -418,11 +414,9 @@ hipError_t launch_cache_fill(const CacheView& c, const int32_t* cu, int64_t T, c
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, const void* k_new,
-                         const void* v_new, hipStream_t st) {
-  const int64_t n = static_cast<int64_t>(c.B) * c.Hkv * (c.d / 8);
-  hipLaunchKernelGGL(cache_append_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     st, c, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new));
+hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t st) {
+  // append + chunked attention, then the merge of the chunks (a kernel
+  // boundary makes the partials of every XCD visible to the merge)
   const dim3 grid(static_cast<unsigned>(a.n_chunks), static_cast<unsigned>(c.Hkv),
                   static_cast<unsigned>(c.B));
   if (c.d == 128) {

@@ -230,6 +230,8 @@ int32_t cache_slot_blocks(int mode, int32_t max_len, int32_t n_sink, int32_t win
 // Arguments of one decode step (one query token per sequence).
 struct DecodeArgs {
   const uint16_t* q;   // [B, Hq, d] bf16
+  const uint16_t* k_new;  // [B, Hkv, d] bf16: the new token's K and V rows
+  const uint16_t* v_new;
   uint16_t* O;         // [B, Hq, d] bf16
   float* lse;          // [B, Hq] or null
   float* o_part;       // [B, Hq, n_chunks, d] chunk partials (workspace)
@@ -244,8 +246,7 @@ constexpr int kDecodeChunkBlocks = 16;
 hipError_t launch_cache_init(const CacheView& c, const int8_t* modes, hipStream_t st);
 hipError_t launch_cache_fill(const CacheView& c, const int32_t* cu, int64_t T, const void* K,
                              const void* V, hipStream_t st);
-hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, const void* k_new,
-                         const void* v_new, hipStream_t st);
+hipError_t launch_decode(const CacheView& c, const DecodeArgs& a, hipStream_t st);
 
 // Arguments of the backward kernels (ea_backward.hip).
 struct BwdArgs {

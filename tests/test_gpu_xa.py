@@ -136,6 +136,7 @@ CASES = [
     ([2000], 8, 2, 128, "FA-XA", [[1, 1]], 1.0, None),
     ([6000], 8, 2, 128, "XA-SSA", [[0, 0]], 0.9, (0.1, 8.0)),
     ([5000, 1100], 16, 4, 128, "FA-XA", [[1, 0, 1, 1], [1, 1, 0, 1]], 0.9, (0.05, 8.0)),
+    ([0, 50, 1300, 7], 8, 2, 128, "XA-SSA", [[0, 0], [0, 1], [0, 0], [1, 0]], 0.9, None),
 ]
 
 
