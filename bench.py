@@ -307,7 +307,7 @@ def bench_dual(args):
                    "sa_kv_heads": int(ly.modes.sum().item())},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "ea_dual_prefill (work list + ea::attention_kernel_bf16<128> + "
+                     "kernel": "ea_dual_prefill (work list + ea::attention_kernel_bf16<128, false> + "
                                "dual_merge_kernel)",
                      "mfma_loop_tflops": probe["tflops"],
                      "frac_of_mfma_loop": round(achieved / probe["tflops"], 4)},
@@ -856,7 +856,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": "ea::attention_kernel_bf16<128>",
+            "kernel": "ea::attention_kernel_bf16<128, false>",
             "avg_launch_ms": round(attn_sum / len(runs), 4),
             "flops_per_launch": round(tot_ef / len(runs), 0),
             "traffic_gbps": (round(traffic / (attn_sum / len(runs) * 1e-3) / 1e9, 1)
