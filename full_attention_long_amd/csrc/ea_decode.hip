@@ -316,53 +316,72 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attn_kernel(CacheView c
 }
 
 // Final O and LSE of one (sequence, query head) from its chunks' partials,
-// one workgroup per 32 of the D dims: the chunk LSEs are reduced to their max
-// and weights by the whole workgroup, then each of its 8 thread groups sums
-// every 8th chunk for the 32 dims and the groups' sums are added.  The
+// one workgroup per 32 of the D dims: thread group q of 8 (32 threads, one
+// per dim) owns chunks q, q + 8, ..., and loads their LSEs and partial rows
+// at once (one memory latency), then the chunk-LSE max and the weight sum are
+// reduced over the workgroup and each group's weighted sums are added.  The
 // (b, 0, 0) workgroup then advances lengths[b] past the new token.
 constexpr int kCombineDims = 32;
 constexpr int kCombineGroups = 256 / kCombineDims;
+constexpr int kCombinePer = 16;  // chunks per thread held in registers
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(CacheView c, DecodeArgs a) {
-  constexpr int kMaxChunks = 2048;
-  __shared__ float wgt[kMaxChunks];
-  __shared__ float red[8];
+  __shared__ float red[2][kCombineGroups];
   __shared__ float acc_s[kCombineGroups][kCombineDims];
   const int hq = blockIdx.x, b = blockIdx.y, slice = blockIdx.z, tid = threadIdx.x;
   const int64_t p0 = (static_cast<int64_t>(b) * a.Hq + hq) * a.n_chunks;
-  const int nc = a.n_chunks;  // <= kMaxChunks, checked on the host
-  float mx = -INFINITY;
-  for (int k = tid; k < nc; k += 256) mx = fmaxf(mx, a.lse_part[p0 + k]);
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (tid % 64 == 0) red[tid / 64] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float ls = 0.f;
-  for (int k = tid; k < nc; k += 256) {
-    const float lk = a.lse_part[p0 + k];
-    const float e = (M == -INFINITY || lk == -INFINITY) ? 0.f : expf(lk - M);
-    wgt[k] = e;
-    ls += e;
-  }
-  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off, 64);
-  if (tid % 64 == 0) red[4 + tid / 64] = ls;
-  __syncthreads();
-  const float L = red[4] + red[5] + red[6] + red[7];
+  const int nc = a.n_chunks;  // <= 2048, checked on the host
   const int dl = tid % kCombineDims, grp = tid / kCombineDims;
   const int dim = slice * kCombineDims + dl;
-  float acc = 0.f;
-#pragma unroll 4
-  for (int k = grp; k < nc; k += kCombineGroups) {
-    const float e = wgt[k];
-    if (e != 0.f) acc += e * a.o_part[(p0 + k) * D + dim];
+  // this thread's chunks: grp + 8 m; the first kCombinePer in registers,
+  // any further ones (nc > 128) read in a second pass
+  float lk[kCombinePer], ok[kCombinePer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < kCombinePer; ++m) {
+    const int k = grp + kCombineGroups * m;
+    lk[m] = k < nc ? a.lse_part[p0 + k] : -INFINITY;
+    ok[m] = k < nc ? a.o_part[(p0 + k) * D + dim] : 0.f;
+    mx = fmaxf(mx, lk[m]);
   }
+  for (int k = grp + kCombineGroups * kCombinePer; k < nc; k += kCombineGroups)
+    mx = fmaxf(mx, a.lse_part[p0 + k]);
+  // lanes of one group hold the same chunks: the group's max is any lane's
+  if (dl == 0) red[0][grp] = mx;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int q = 1; q < kCombineGroups; ++q) M = fmaxf(M, red[0][q]);
+  float ls = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int m = 0; m < kCombinePer; ++m) {
+      if (lk[m] != -INFINITY) {
+        const float e = expf(lk[m] - M);
+        ls += e;
+        acc += e * ok[m];
+      }
+    }
+    for (int k = grp + kCombineGroups * kCombinePer; k < nc; k += kCombineGroups) {
+      const float l = a.lse_part[p0 + k];
+      if (l != -INFINITY) {
+        const float e = expf(l - M);
+        ls += e;
+        acc += e * a.o_part[(p0 + k) * D + dim];
+      }
+    }
+  }
+  if (dl == 0) red[1][grp] = ls;
   acc_s[grp][dl] = acc;
   __syncthreads();
   if (grp == 0) {
-    float o = 0.f;
+    float L = 0.f, o = 0.f;
 #pragma unroll
-    for (int g = 0; g < kCombineGroups; ++g) o += acc_s[g][dl];
+    for (int q = 0; q < kCombineGroups; ++q) {
+      L += red[1][q];
+      o += acc_s[q][dl];
+    }
     const int64_t orow = (static_cast<int64_t>(b) * a.Hq + hq) * D;
     a.O[orow + dim] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(L > 0.f ? o / L : 0.f));
     if (dim == 0 && a.lse) a.lse[static_cast<int64_t>(b) * a.Hq + hq] = L > 0.f ? M + logf(L) : -INFINITY;
