@@ -93,7 +93,9 @@ def test_decode_full_sequence_outputs_zero_and_keeps_length():
 
 
 def test_decode_full_size_128k():
-    # the headline layer's K/V as the prompt, then 3 decode steps
+    # the headline layer's K/V as the prompt, then 3 decode steps; max_len
+    # L + 64 makes 129 chunks of 16 blocks and the new tokens land in the last
+    # one, past the 128 chunks the merge kernel holds in registers
     wl = WORKLOADS["qwen4b_s128k_sa6"]
     note("decode 128K: generating")
     c = gen.build_case(wl)
