@@ -8,16 +8,18 @@
 // tokens); Fig. 3(b) paragraph for the 0 = FA / 1 = SA convention.
 //
 // The work is tiny (200 rows of K, ~0.14-0.27M weights) and latency bound:
-// pooling reads coalesced rows of K; each matrix-vector product gives one
-// output row per wave with the lanes striding the contiguous input axis and a
-// butterfly reduction across the wave.
+// pooling reads coalesced rows of K; each matrix-vector product gives
+// kRowsPerWave output rows per wave at a time, the lanes striding the
+// contiguous input axis, so the loads of all those rows are in flight
+// together, then one butterfly reduction across the wave per row.
 #include "ea_internal.h"
 
 namespace ea {
 namespace {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRowsPerWave = 8;
 
 __device__ __forceinline__ float load_elem(const void* p, int64_t i, bool bf16) {
   if (bf16) {
@@ -41,14 +43,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ void matvec(const float* __restrict__ W, const float* __restrict__ bias,
                        const float* x, float* out, int rows, int cols, bool act) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  for (int r = wave; r < rows; r += kRouteWaves) {
-    const float* wr = W + static_cast<int64_t>(r) * cols;
-    float acc = 0.f;
-    for (int c = lane; c < cols; c += 64) acc += wr[c] * x[c];
-    acc = wave_sum(acc);
+  for (int r0 = wave * kRowsPerWave; r0 < rows; r0 += kRouteWaves * kRowsPerWave) {
+    float acc[kRowsPerWave];
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) acc[j] = 0.f;
+#pragma unroll 4
+    for (int c = lane; c < cols; c += 64) {
+      const float xv = x[c];
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j)
+        if (r0 + j < rows) acc[j] += W[static_cast<int64_t>(r0 + j) * cols + c] * xv;
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) acc[j] = wave_sum(acc[j]);
     if (lane == 0) {
-      float y = acc + bias[r];
-      out[r] = act ? gelu_erf(y) : y;
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j) {
+        if (r0 + j < rows) {
+          const float y = acc[j] + bias[r0 + j];
+          out[r0 + j] = act ? gelu_erf(y) : y;
+        }
+      }
     }
   }
 }
@@ -89,6 +104,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int c = threadIdx.x % d, stripe = threadIdx.x / d;
   float acc = 0.f;
   if (stripe < n_stripes) {
+#pragma unroll 8
     for (int i = stripe; i < n_rows; i += n_stripes) {
       const int row = i < head_end ? i : tail_beg + (i - head_end);
       acc += load_elem(K, (static_cast<int64_t>(s0 + row) * Hkv + g) * d + c, bf16);
