@@ -56,7 +56,7 @@ constexpr float kSumLimit = 1048576.0f;
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-constexpr int kValuPerMfma = 8;
+constexpr int kValuPerMfma = 5;
 constexpr int kDsAhead = 4;
 constexpr int kPvAhead = 4;
 // word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data, no swizzle)
