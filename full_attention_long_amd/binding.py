@@ -179,6 +179,48 @@ def _dev(t, name):
     return t
 
 
+def _meta(t, name, dtypes=None, shape=None, ndim=None):
+    """Checks a tensor argument's dtype and shape.  The C ABI receives bare
+    pointers, so this is the last place a buffer of the wrong size or element
+    type can be refused before a kernel reads or writes past its end."""
+    if t is None:
+        raise EAError(EA_ERR_INVALID_ARG, f"{name} is required")
+    if ndim is not None and t.dim() != ndim:
+        raise EAError(EA_ERR_INVALID_ARG, f"{name} must have {ndim} dimensions (got {t.dim()})")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise EAError(EA_ERR_INVALID_ARG, f"{name} must be of dtype {' or '.join(map(str, dtypes))} "
+                                          f"(got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise EAError(EA_ERR_INVALID_ARG, f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _float_types():
+    import torch
+    return (torch.bfloat16, torch.float32)
+
+
+def _check_cu(cu_seqlens):
+    """cu_seqlens: int32 [B + 1], B >= 1; returns B."""
+    import torch
+    _meta(cu_seqlens, "cu_seqlens", (torch.int32,), ndim=1)
+    if cu_seqlens.numel() < 2:
+        raise EAError(EA_ERR_INVALID_ARG, "cu_seqlens must hold B + 1 >= 2 offsets")
+    return cu_seqlens.numel() - 1
+
+
+def _check_qkv(Q, K, V):
+    """Q [T, Hq, d] and K, V [T, Hkv, d] of one floating dtype; returns T, Hq, Hkv, d."""
+    _meta(Q, "Q", _float_types(), ndim=3)
+    T, Hq, d = Q.shape
+    _meta(K, "K", (Q.dtype,), ndim=3)
+    Hkv = K.shape[1]
+    _meta(K, "K", shape=(T, Hkv, d))
+    if V is not None:
+        _meta(V, "V", (Q.dtype,), shape=(T, Hkv, d))
+    return T, Hq, Hkv, d
+
+
 def ea_abi_version() -> int:
     return int(lib().ea_abi_version())
 
@@ -191,10 +233,22 @@ def ea_route(K, cu_seqlens, weights: dict, *, pool_len: int = 100, modes=None, l
              with_logits: bool = True, stream=None):
     """Hard FA/SA modes (int8 [B, Hkv]) and logits (float32 [B, Hkv, 2]) from K [T, Hkv, d]."""
     import torch
+    _meta(K, "K", _float_types(), ndim=3)
+    B = _check_cu(cu_seqlens)
+    Hkv, d = K.shape[1], K.shape[2]
+    f32 = (torch.float32,)
+    w1 = _meta(weights.get("w1"), "w1", f32, ndim=2)
+    w3 = _meta(weights.get("w3"), "w3", f32, ndim=2)
+    H1, H3 = w1.shape[0], w3.shape[0]
+    for k, shape in [("w1", (H1, d)), ("b1", (H1,)), ("w2", (d, H1)), ("b2", (d,)),
+                     ("w3", (H3, d)), ("b3", (H3,)), ("w4", (2, H3)), ("b4", (2,))]:
+        _meta(weights.get(k), k, f32, shape=shape)
+    if modes is not None:
+        _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    if logits is not None:
+        _meta(logits, "logits", f32, shape=(B, Hkv, 2))
     _dev(K, "K")
     _dev(cu_seqlens, "cu_seqlens")
-    B = cu_seqlens.numel() - 1
-    Hkv, d = K.shape[1], K.shape[2]
     w = {k: _dev(weights[k], k) for k in ["w1", "b1", "w2", "b2", "w3", "b3", "w4", "b4"]}
     desc = RouterDesc(d, w["w1"].shape[0], w["w3"].shape[0], pool_len,
                       *[w[k].data_ptr() for k in ["w1", "b1", "w2", "b2", "w3", "b3", "w4", "b4"]])
@@ -214,11 +268,19 @@ def ea_hybrid_prefill_workspace_size(B, total_tokens, max_seqlen, Hq, Hkv, head_
 
 def _prefill_args(Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen):
     import torch
+    T, Hq, Hkv, d = _check_qkv(Q, K, V)
+    B = _check_cu(cu_seqlens)
+    _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    if out is not None:
+        _meta(out, "out", (Q.dtype,), shape=Q.shape)
+    if lse is not None:
+        _meta(lse, "lse", (torch.float32,), shape=(Hq, T))
+    if workspace is not None:
+        _meta(workspace, "workspace", (torch.uint8,), ndim=1)
     for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (modes, "modes"), (cu_seqlens, "cu_seqlens")]:
         _dev(t, n)
-    T, Hq, d = Q.shape
-    Hkv = K.shape[1]
-    B = cu_seqlens.numel() - 1
+    if workspace is not None:
+        _dev(workspace, "workspace")
     code = _dtype_code(Q)
     if out is None:
         out = torch.empty_like(Q)
@@ -249,10 +311,13 @@ def ea_hybrid_prefill_plan(modes, cu_seqlens, total_tokens: int, max_seqlen: int
                            window_blocks: int = 0, keep_fraction: float = 0.2,
                            softmax_scale: float = 0.0, block: int = 64, stream=None):
     """Build the cost-ordered work list into ``workspace`` (a uint8 device tensor)."""
+    import torch
+    B = _check_cu(cu_seqlens)
+    _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    _meta(workspace, "workspace", (torch.uint8,), ndim=1)
     _dev(modes, "modes")
     _dev(cu_seqlens, "cu_seqlens")
     _dev(workspace, "workspace")
-    B = cu_seqlens.numel() - 1
     sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
     _check(lib().ea_hybrid_prefill_plan(_ptr(modes), _ptr(cu_seqlens), B, total_tokens, max_seqlen,
                                         Hq, Hkv, head_dim, dtype_code, ctypes.byref(sp),
@@ -265,7 +330,6 @@ def ea_hybrid_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace
                           softmax_scale: float = 0.0, block: int = 64, out=None, lse=None,
                           with_lse: bool = True, stream=None):
     """The attention launch alone, over a workspace ``ea_hybrid_prefill_plan`` filled."""
-    _dev(workspace, "workspace")
     T, Hq, Hkv, d, B, code, out, lse, workspace = _prefill_args(
         Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen)
     sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
@@ -293,9 +357,9 @@ def ea_xa_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, head_config="X
     tensors, nqb = ceil(max_seqlen / xa_block)) receive the XA heads' block
     masses and keep flags when given."""
     import torch
-    T, Hq, d = Q.shape
-    Hkv = K.shape[1]
-    B = cu_seqlens.numel() - 1
+    T, Hq, Hkv, d = _check_qkv(Q, K, V)
+    B = _check_cu(cu_seqlens)
+    _check_xa_outputs(mass, keep, B, Hq, max_seqlen, xa_block)
     code = _dtype_code(Q)
     if workspace is None:
         need = ea_xa_prefill_workspace_size(B, T, max_seqlen, Hq, Hkv, d, code)
@@ -314,6 +378,15 @@ def ea_xa_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, head_config="X
     return out, lse
 
 
+def _check_xa_outputs(mass, keep, B, Hq, max_seqlen, xa_block):
+    """mass float32 / keep uint8 [B, Hq, nqb, nqb], nqb = ceil(max_seqlen / xa_block)."""
+    import torch
+    nqb = (max_seqlen + xa_block - 1) // xa_block if xa_block > 0 else 0
+    for t, n, dt in [(mass, "mass", torch.float32), (keep, "keep", torch.uint8)]:
+        if t is not None:
+            _meta(t, n, (dt,), shape=(B, Hq, nqb, nqb))
+
+
 def _xa_params(head_config, threshold, xa_block, stride):
     cfg = HEAD_CONFIGS[head_config] if isinstance(head_config, str) else int(head_config)
     return XAParams(xa_block, stride, threshold, cfg)
@@ -326,10 +399,16 @@ def ea_xa_prefill_plan(Q, K, modes, cu_seqlens, max_seqlen: int, workspace, *,
                        mass=None, keep=None, stream=None):
     """XA selection and work list into ``workspace`` (uint8 device tensor of
     ``ea_xa_prefill_workspace_size`` bytes)."""
+    import torch
+    T, Hq, Hkv, d = _check_qkv(Q, K, None)
+    B = _check_cu(cu_seqlens)
+    _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    _meta(workspace, "workspace", (torch.uint8,), ndim=1)
+    _check_xa_outputs(mass, keep, B, Hq, max_seqlen, xa_block)
     for t, n in [(Q, "Q"), (K, "K"), (modes, "modes"), (cu_seqlens, "cu_seqlens"),
-                 (workspace, "workspace")]:
-        _dev(t, n)
-    T, Hq, d = Q.shape
+                 (workspace, "workspace"), (mass, "mass"), (keep, "keep")]:
+        if t is not None or n not in ("mass", "keep"):
+            _dev(t, n)
     sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
     xp = _xa_params(head_config, threshold, xa_block, stride)
     _check(lib().ea_xa_prefill_plan(_ptr(Q), _ptr(K), _dtype_code(Q), _ptr(modes), _ptr(cu_seqlens),
@@ -345,7 +424,6 @@ def ea_xa_prefill_run(Q, K, V, modes, cu_seqlens, max_seqlen: int, workspace, *,
                       keep_fraction: float = 0.2, softmax_scale: float = 0.0, block: int = 64,
                       out=None, lse=None, with_lse: bool = True, stream=None):
     """The attention launch over a workspace ``ea_xa_prefill_plan`` filled."""
-    _dev(workspace, "workspace")
     T, Hq, Hkv, d, B, code, out, lse, workspace = _prefill_args(
         Q, K, V, modes, cu_seqlens, out, lse, with_lse, workspace, max_seqlen)
     sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
@@ -369,12 +447,18 @@ def ea_hybrid_backward(Q, K, V, O, dO, lse, modes, cu_seqlens, max_seqlen: int, 
     """(dQ, dK, dV) of the hybrid layer for the upstream gradient dO, given the
     forward's O and LSE (bf16 tensors; LSE float32 [Hq, T])."""
     import torch
+    T, Hq, Hkv, d = _check_qkv(Q, K, V)
+    B = _check_cu(cu_seqlens)
+    _meta(O, "O", (Q.dtype,), shape=Q.shape)
+    _meta(dO, "dO", (Q.dtype,), shape=Q.shape)
+    _meta(lse, "lse", (torch.float32,), shape=(Hq, T))
+    _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    for t, n, like in [(dQ, "dQ", Q), (dK, "dK", K), (dV, "dV", V)]:
+        if t is not None:
+            _meta(t, n, (Q.dtype,), shape=like.shape)
     for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (O, "O"), (dO, "dO"), (lse, "lse"),
                  (modes, "modes"), (cu_seqlens, "cu_seqlens")]:
         _dev(t, n)
-    T, Hq, d = Q.shape
-    Hkv = K.shape[1]
-    B = cu_seqlens.numel() - 1
     code = _dtype_code(Q)
     dQ = torch.empty_like(Q) if dQ is None else dQ
     dK = torch.empty_like(K) if dK is None else dK
@@ -399,12 +483,20 @@ def ea_router_logit_grad(dO, O_fa, O_sa, cu_seqlens, max_seqlen: int, r_soft, ta
     """(dz, dr) float32 [B, Hkv, 2]: the routing logits' gradient through the
     straight-through estimator and the Gumbel-Softmax."""
     import torch
+    _meta(dO, "dO", _float_types(), ndim=3)
+    T, Hq, d = dO.shape
+    _meta(O_fa, "O_fa", (dO.dtype,), shape=dO.shape)
+    _meta(O_sa, "O_sa", (dO.dtype,), shape=dO.shape)
+    B = _check_cu(cu_seqlens)
+    _meta(r_soft, "r_soft", (torch.float32,), ndim=3)
+    Hkv = r_soft.shape[1]
+    _meta(r_soft, "r_soft", shape=(B, Hkv, 2))
+    for t, n in [(dz, "dz"), (dr, "dr")]:
+        if t is not None:
+            _meta(t, n, (torch.float32,), shape=(B, Hkv, 2))
     for t, n in [(dO, "dO"), (O_fa, "O_fa"), (O_sa, "O_sa"), (cu_seqlens, "cu_seqlens"),
                  (r_soft, "r_soft")]:
         _dev(t, n)
-    T, Hq, d = dO.shape
-    B = cu_seqlens.numel() - 1
-    Hkv = r_soft.shape[1]
     dz = torch.empty_like(r_soft) if dz is None else dz
     if dr is None and with_dr:
         dr = torch.empty_like(r_soft)
@@ -431,6 +523,10 @@ def ea_gumbel_route(logits, tau: float, *, gumbel=None, r_soft=None, modes=None,
         _dev(gumbel, "gumbel")
         if gumbel.shape != logits.shape or gumbel.dtype != torch.float32:
             raise ValueError("gumbel must be float32 of the logits' shape")
+    if r_soft is not None:
+        _meta(r_soft, "r_soft", (torch.float32,), shape=logits.shape)
+    if modes is not None:
+        _meta(modes, "modes", (torch.int8,), shape=logits.shape[:-1])
     n = logits.numel() // 2
     if modes is None:
         modes = torch.empty(logits.shape[:-1], dtype=torch.int8, device=logits.device)
@@ -456,13 +552,20 @@ def ea_dual_prefill(Q, K, V, cu_seqlens, max_seqlen: int, *, modes=None, n_sink:
     hard decision's output per (sequence, KV head)) only when ``modes`` is
     given, else None."""
     import torch
+    T, Hq, Hkv, d = _check_qkv(Q, K, V)
+    B = _check_cu(cu_seqlens)
+    if modes is not None:
+        _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    for t, n in [(out, "out"), (out_fa, "out_fa"), (out_sa, "out_sa")]:
+        if t is not None:
+            _meta(t, n, (Q.dtype,), shape=Q.shape)
+    for t, n in [(lse_fa, "lse_fa"), (lse_sa, "lse_sa")]:
+        if t is not None:
+            _meta(t, n, (torch.float32,), shape=(Hq, T))
     for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (cu_seqlens, "cu_seqlens")]:
         _dev(t, n)
     if modes is not None:
         _dev(modes, "modes")
-    T, Hq, d = Q.shape
-    Hkv = K.shape[1]
-    B = cu_seqlens.numel() - 1
     code = _dtype_code(Q)
     if out is None and modes is not None:
         out = torch.empty_like(Q)
@@ -491,6 +594,9 @@ def ea_kvcache_bytes(desc: KVCacheDesc, modes_host) -> int:
 
 
 def ea_kvcache_init(desc: KVCacheDesc, modes, cache, *, stream=None):
+    import torch
+    _meta(modes, "modes", (torch.int8,), shape=(desc.B, desc.Hkv))
+    _meta(cache, "cache", (torch.uint8,), ndim=1)
     _dev(modes, "modes")
     _dev(cache, "cache")
     _check(lib().ea_kvcache_init(ctypes.byref(desc), _ptr(modes), _ptr(cache), cache.numel(),
@@ -499,6 +605,12 @@ def ea_kvcache_init(desc: KVCacheDesc, modes, cache, *, stream=None):
 
 
 def ea_kvcache_prefill(desc: KVCacheDesc, cache, K, V, cu_seqlens, *, stream=None):
+    import torch
+    _meta(cache, "cache", (torch.uint8,), ndim=1)
+    _meta(K, "K", (torch.bfloat16,), ndim=3)
+    _meta(K, "K", shape=(K.shape[0], desc.Hkv, desc.head_dim))
+    _meta(V, "V", (torch.bfloat16,), shape=K.shape)
+    _meta(cu_seqlens, "cu_seqlens", (torch.int32,), shape=(desc.B + 1,))
     for t, n in [(cache, "cache"), (K, "K"), (V, "V"), (cu_seqlens, "cu_seqlens")]:
         _dev(t, n)
     _check(lib().ea_kvcache_prefill(ctypes.byref(desc), _ptr(cache), cache.numel(), _ptr(K),
@@ -515,9 +627,18 @@ def ea_decode_step(desc: KVCacheDesc, cache, q, k_new, v_new, *, softmax_scale: 
     """Append (k_new, v_new) [B, Hkv, d] at each sequence's length and attend
     with q [B, Hq, d]; returns (O [B, Hq, d] bf16, LSE float32 [B, Hq])."""
     import torch
+    _meta(cache, "cache", (torch.uint8,), ndim=1)
+    _meta(q, "q", (torch.bfloat16,), ndim=3)
+    Hq = q.shape[1]
+    _meta(q, "q", shape=(desc.B, Hq, desc.head_dim))
+    _meta(k_new, "k_new", (torch.bfloat16,), shape=(desc.B, desc.Hkv, desc.head_dim))
+    _meta(v_new, "v_new", (torch.bfloat16,), shape=(desc.B, desc.Hkv, desc.head_dim))
+    if out is not None:
+        _meta(out, "out", (torch.bfloat16,), shape=q.shape)
+    if lse is not None:
+        _meta(lse, "lse", (torch.float32,), shape=(desc.B, Hq))
     for t, n in [(cache, "cache"), (q, "q"), (k_new, "k_new"), (v_new, "v_new")]:
         _dev(t, n)
-    Hq = q.shape[1]
     if out is None:
         out = torch.empty_like(q)
     if lse is None and with_lse:
