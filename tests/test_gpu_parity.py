@@ -73,6 +73,20 @@ def test_route_varlen_edge_lengths(dtype, d):
     assert (logits[np.array(lengths) == 0] == 0).all()
 
 
+@pytest.mark.parametrize("d,task_hidden,router_hidden", [(64, 100, 7), (128, 1000, 65), (96, 37, 3)])
+def test_route_odd_mlp_widths(d, task_hidden, router_hidden):
+    # widths that fill neither the eight output rows a wave takes per pass
+    # nor the 64-lane stride over the input axis
+    c = gen.custom_case(13, [333, 1200], 4, 2, d, "bf16", task_hidden=task_hidden,
+                        router_hidden=router_hidden, w_std=0.2)
+    note(f"route widths d={d} task={task_hidden} router={router_hidden}")
+    modes, logits = gpu_route(c)
+    ref_modes, ref_z = orc.route(c.k_f32(), c.cu_seqlens, c.weights, c.pool_len)
+    assert np.abs(logits - ref_z).max() <= 1e-5
+    posed = np.abs(ref_z[..., 0] - ref_z[..., 1]) > 1e-4
+    np.testing.assert_array_equal(modes[posed], ref_modes[posed])
+
+
 def test_route_reads_only_boundary_rows():
     c = gen.custom_case(12, [1000, 700], 4, 2, 128, "bf16", w_std=0.2)
     note("route locality")
