@@ -195,6 +195,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   auto block = [&](int kb, const uint16_t* kr_, const uint16_t* vr_, const uint16_t* kt_) {
     f32x16 s0, s1, p0v, p1v;
     rowmm(kr_, qf, s0, s1);
+    // dP^T needs only LDS operands: issued here, its products run in the
+    // matrix pipe while the exponentials below wait on and consume S
+    rowmm(vr_, of, p0v, p1v);
     // a block every row of the tile sees (the common case) skips the
     // per-element visibility test
     if (block_full(mode, kb, p0, qb0, qb1, ns, w)) {
@@ -213,7 +216,6 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
         s1[i] = v1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lrow)) : 0.f;
       }
     }
-    rowmm(vr_, of, p0v, p1v);  // dP^T
     bf16x8 dsb[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
