@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     ea_hybrid_prefill_run,
     ea_hybrid_prefill_workspace_size,
     ea_last_error,
+    ea_workspace_status,
     ea_mfma_probe,
     ea_route,
     ea_router_logit_grad,

@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.ea_abi_version.argtypes = []
     L.ea_last_error.restype = ctypes.c_char_p
     L.ea_last_error.argtypes = []
+    L.ea_workspace_status.restype = i32
+    L.ea_workspace_status.argtypes = [vp, sz, vp]
     L.ea_route.restype = i32
     L.ea_route.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(RouterDesc), vp, vp, vp]
     L.ea_hybrid_prefill_workspace_size.restype = sz
@@ -227,6 +229,15 @@ def ea_abi_version() -> int:
 
 def ea_last_error() -> str:
     return lib().ea_last_error().decode()
+
+
+def ea_workspace_status(workspace, stream=None):
+    """Raise EAError if the plan in ``workspace`` (uint8 device tensor) failed
+    the planner's device-content checks; waits for ``stream``."""
+    import torch
+    _meta(workspace, "workspace", (torch.uint8,), ndim=1)
+    _dev(workspace, "workspace")
+    _check(lib().ea_workspace_status(_ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def ea_route(K, cu_seqlens, weights: dict, *, pool_len: int = 100, modes=None, logits=None,

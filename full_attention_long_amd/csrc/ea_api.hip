@@ -2,8 +2,11 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "ea_internal.h"
 
@@ -27,6 +30,67 @@ ea_status ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// EA_VALIDATE=1 (any value but empty or "0") makes every call that plans a
+// work list, or runs one, wait for the planner's device-content checks and
+// return their verdict; without it the checks still run on the device and
+// keep every later kernel of the call from touching memory, but nothing
+// waits for them (ea_workspace_status reads the verdict later).
+// The variable is read at every call, so a process can switch it.
+bool validate_on() {
+  const char* e = getenv("EA_VALIDATE");
+  return e && e[0] && strcmp(e, "0") != 0;
+}
+
+std::string describe_meta_error(int32_t err) {
+  std::string m;
+  auto add = [&](int32_t bit, const char* what) {
+    if (err & bit) m += (m.empty() ? "" : "; ") + std::string(what);
+  };
+  add(ea::kErrCuStart, "cu_seqlens[0] != 0");
+  add(ea::kErrCuOrder, "cu_seqlens decreases");
+  add(ea::kErrCuEnd, "cu_seqlens[B] != total_tokens");
+  add(ea::kErrSeqLen, "a sequence is longer than max_seqlen");
+  add(ea::kErrMode, "a mode value is not 0 or 1");
+  return m;
+}
+
+// Waits for `stream`, then reads the planner's verdict from the workspace
+// header (the header sits at offset 0 of every planned workspace).
+ea_status workspace_verdict(const void* workspace, void* stream) {
+  int32_t err = 0;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&err, static_cast<const char*>(workspace) + sizeof(int32_t) * ea::kMetaError,
+                                sizeof(err), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "reading the workspace header failed: %s", hipGetErrorString(e));
+  if (err != 0)
+    return fail(EA_ERR_INVALID_ARG, "invalid device contents: %s", describe_meta_error(err).c_str());
+  return EA_OK;
+}
+
+// Host-side checks of cu_seqlens for the calls that take no workspace
+// (router, KV-cache fill), under EA_VALIDATE only: copies the B + 1 values.
+// total_tokens < 0 skips the end check, max_len < 0 the length check.
+ea_status host_check_cu(const int32_t* cu, int32_t B, int64_t total_tokens, int64_t max_len,
+                        void* stream) {
+  std::vector<int32_t> h(static_cast<size_t>(B) + 1);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "reading cu_seqlens failed: %s", hipGetErrorString(e));
+  int32_t err = 0;
+  if (h[0] != 0) err |= ea::kErrCuStart;
+  if (total_tokens >= 0 && h[B] != total_tokens) err |= ea::kErrCuEnd;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t len = static_cast<int64_t>(h[b + 1]) - h[b];
+    if (len < 0) err |= ea::kErrCuOrder;
+    if (max_len >= 0 && len > max_len) err |= ea::kErrSeqLen;
+  }
+  if (err != 0)
+    return fail(EA_ERR_INVALID_ARG, "invalid device contents: %s", describe_meta_error(err).c_str());
+  return EA_OK;
+}
 
 // Validates the sizes shared by the workspace query and the prefill call.
 ea_status check_shape(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
@@ -74,8 +138,12 @@ ea_status check_prefill(int32_t B, int64_t T, int32_t max_seqlen, int32_t Hq, in
   if (!p) return fail(EA_ERR_INVALID_ARG, "null sparsity params");
   if (p->block != ea::kBlock)
     return fail(EA_ERR_UNSUPPORTED, "sparsity block must be %d (got %d)", ea::kBlock, p->block);
-  if (p->n_sink_blocks < 0) return fail(EA_ERR_INVALID_ARG, "n_sink_blocks must be >= 0");
-  if (p->window_blocks < 0) return fail(EA_ERR_INVALID_ARG, "window_blocks must be >= 0");
+  if (p->n_sink_blocks < 0 || p->n_sink_blocks > ea::kMaxGeomBlocks)
+    return fail(EA_ERR_INVALID_ARG, "n_sink_blocks must be in [0, %d] (got %d)", ea::kMaxGeomBlocks,
+                p->n_sink_blocks);
+  if (p->window_blocks < 0 || p->window_blocks > ea::kMaxGeomBlocks)
+    return fail(EA_ERR_INVALID_ARG, "window_blocks must be in [0, %d] (got %d)", ea::kMaxGeomBlocks,
+                p->window_blocks);
   if (p->window_blocks == 0 && !(p->keep_fraction > 0.f && p->keep_fraction <= 1.f))
     return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1] (got %g)", (double)p->keep_fraction);
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
@@ -108,6 +176,15 @@ extern "C" {
 
 int32_t ea_abi_version(void) { return EA_ABI_VERSION; }
 
+ea_status ea_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (workspace_bytes < sizeof(int32_t) * ea::kMetaSlots)
+    return fail(EA_ERR_WORKSPACE, "workspace of at least %zu bytes expected (got %zu)",
+                sizeof(int32_t) * ea::kMetaSlots, workspace_bytes);
+  ea_status st = workspace_verdict(workspace, stream);
+  return st != EA_OK ? st : ok();
+}
+
 const char* ea_last_error(void) { return g_err.c_str(); }
 
 ea_status ea_route(const void* K, ea_dtype dtype, const int32_t* cu_seqlens, int32_t B,
@@ -126,6 +203,10 @@ ea_status ea_route(const void* K, ea_dtype dtype, const int32_t* cu_seqlens, int
   if (r->pool_len < 1) return fail(EA_ERR_INVALID_ARG, "pool_len must be >= 1 (got %d)", r->pool_len);
   if (!r->w1 || !r->b1 || !r->w2 || !r->b2 || !r->w3 || !r->b3 || !r->w4 || !r->b4)
     return fail(EA_ERR_INVALID_ARG, "null router weight pointer");
+  if (validate_on()) {
+    ea_status v = host_check_cu(cu_seqlens, B, -1, -1, stream);
+    if (v != EA_OK) return v;
+  }
   hipError_t e = ea::launch_route(K, dtype == EA_BF16, cu_seqlens, B, Hkv, *r, modes, logits,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(EA_ERR_HIP, "route launch failed: %s", hipGetErrorString(e));
@@ -156,6 +237,7 @@ ea_status ea_hybrid_prefill_plan(const int8_t* modes, const int32_t* cu_seqlens,
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, static_cast<char*>(workspace),
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(EA_ERR_HIP, "work-list launch failed: %s", hipGetErrorString(e));
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
   return ok();
 }
 
@@ -172,6 +254,7 @@ ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_
   if (st != EA_OK) return st;
   if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
   if (total_tokens == 0) return ok();
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
   hipError_t e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr},
                                       ws, static_cast<char*>(const_cast<void*>(workspace)),
                                       static_cast<hipStream_t>(stream));
@@ -195,9 +278,10 @@ ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtyp
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
-  if (e == hipSuccess)
-    e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr}, ws,
-                             base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
+  e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr}, ws,
+                           base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -245,10 +329,13 @@ ea_status ea_dual_prefill(const void* Q, const void* K, const void* V, ea_dtype 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "dual prefill launch failed: %s", hipGetErrorString(e));
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
+  e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O_sa, lse_sa, O_fa, lse_fa}, ws,
+                           base, hs);
   if (e == hipSuccess)
-    e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O_sa, lse_sa, O_fa, lse_fa},
-                             ws, base, hs);
-  if (e == hipSuccess) e = ea::launch_dual_merge(s, cu_seqlens, modes, O_sa, lse_sa, O_fa, lse_fa, O, hs);
+    e = ea::launch_dual_merge(s, cu_seqlens, modes, O_sa, lse_sa, O_fa, lse_fa, O,
+                              reinterpret_cast<const int32_t*>(base + ws.meta), hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "dual prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -316,9 +403,12 @@ ea_status ea_xa_prefill_plan(const void* Q, const void* K, ea_dtype dtype, const
   if (total_tokens == 0) return ok();
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
-  hipError_t e = ea::launch_xa_plan(s, g, xa->threshold, Q, K, modes, cu_seqlens, ws, base, xa_mass,
-                                    xa_keep, hs);
-  if (e == hipSuccess) e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  // setup (with the device-content checks) first: the selection reads its verdict
+  hipError_t e = ea::launch_setup(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "XA plan launch failed: %s", hipGetErrorString(e));
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
+  e = ea::launch_xa_plan(s, g, xa->threshold, Q, K, modes, cu_seqlens, ws, base, xa_mass, xa_keep, hs);
+  if (e == hipSuccess) e = ea::launch_items(s, g, modes, cu_seqlens, ws, base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "XA plan launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -337,6 +427,7 @@ ea_status ea_xa_prefill_run(const void* Q, const void* K, const void* V, ea_dtyp
   if (st != EA_OK) return st;
   if ((st = check_tensors(Q, K, V, O)) != EA_OK) return st;
   if (total_tokens == 0) return ok();
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
   hipError_t e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr},
                                       ws, static_cast<char*>(const_cast<void*>(workspace)),
                                       static_cast<hipStream_t>(stream));
@@ -360,9 +451,11 @@ ea_status ea_xa_prefill(const void* Q, const void* K, const void* V, ea_dtype dt
   if (total_tokens == 0) return ok();
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
-  hipError_t e = ea::launch_xa_plan(s, g, xa->threshold, Q, K, modes, cu_seqlens, ws, base, xa_mass,
-                                    xa_keep, hs);
-  if (e == hipSuccess) e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
+  hipError_t e = ea::launch_setup(s, g, modes, cu_seqlens, ws, base, hs);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "XA prefill launch failed: %s", hipGetErrorString(e));
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
+  e = ea::launch_xa_plan(s, g, xa->threshold, Q, K, modes, cu_seqlens, ws, base, xa_mass, xa_keep, hs);
+  if (e == hipSuccess) e = ea::launch_items(s, g, modes, cu_seqlens, ws, base, hs);
   if (e == hipSuccess)
     e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr}, ws,
                              base, hs);
@@ -384,8 +477,10 @@ ea_status check_cache_desc(const ea_kvcache_desc* c) {
   if (c->max_len < 1) return fail(EA_ERR_INVALID_ARG, "max_len must be >= 1");
   if (c->max_len > 2048 * ea::kDecodeChunkBlocks * ea::kBlock)
     return fail(EA_ERR_UNSUPPORTED, "max_len must be <= %d", 2048 * ea::kDecodeChunkBlocks * ea::kBlock);
-  if (c->n_sink_blocks < 0 || c->window_blocks < 0)
-    return fail(EA_ERR_INVALID_ARG, "n_sink_blocks and window_blocks must be >= 0");
+  if (c->n_sink_blocks < 0 || c->window_blocks < 0 || c->n_sink_blocks > ea::kMaxGeomBlocks ||
+      c->window_blocks > ea::kMaxGeomBlocks)
+    return fail(EA_ERR_INVALID_ARG, "n_sink_blocks and window_blocks must be in [0, %d]",
+                ea::kMaxGeomBlocks);
   if (c->window_blocks == 0 && !(c->keep_fraction > 0.f && c->keep_fraction <= 1.f))
     return fail(EA_ERR_INVALID_ARG, "keep_fraction must be in (0, 1]");
   return EA_OK;
@@ -462,6 +557,8 @@ ea_status ea_kvcache_prefill(const ea_kvcache_desc* desc, void* cache, size_t by
   if (!aligned16(K) || !aligned16(V)) return fail(EA_ERR_INVALID_ARG, "K and V must be 16-byte aligned");
   if (total_tokens < 0 || total_tokens >= (int64_t(1) << 31))
     return fail(EA_ERR_INVALID_ARG, "total_tokens must be in [0, 2^31)");
+  if (validate_on() && (st = host_check_cu(cu_seqlens, desc->B, total_tokens, desc->max_len, stream)) != EA_OK)
+    return st;
   hipError_t e = ea::launch_cache_fill(cache_view(desc, cache, bytes), cu_seqlens, total_tokens,
                                        K, V, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(EA_ERR_HIP, "cache fill launch failed: %s", hipGetErrorString(e));
@@ -563,6 +660,7 @@ ea_status ea_hybrid_backward(const void* Q, const void* K, const void* V, const 
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "work-list launch failed: %s", hipGetErrorString(e));
+  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
   ea::BwdArgs a{};
   a.Q = static_cast<const uint16_t*>(Q);
   a.K = static_cast<const uint16_t*>(K);

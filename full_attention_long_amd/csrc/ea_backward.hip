@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   const int64_t rest = item / a.npair;
   const int g = static_cast<int>(rest % a.Hkv);
   const int b = static_cast<int>(rest / a.Hkv);
+  if (a.meta[kMetaStamp] != a.stamp) return;  // the planner rejected the device contents
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
   if (pair * kDkvKeys >= L) return;
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(256) void dkv_items_kernel(BwdArgs a, int32_t maxco
   const int b = static_cast<int>(rest / a.Hkv);
   const int L = a.cu[b + 1] - a.cu[b];
   const uint32_t last = static_cast<uint32_t>(maxcost >> kCostBandShift) + 1;
-  if (pair * kDkvKeys >= L) {
+  if (a.meta[kMetaStamp] != a.stamp || pair * kDkvKeys >= L) {
     keys[x] = last;
     return;
   }

@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(CacheView c, const int3
     const int b = find_seq(cu, c.B, t);
     const int L = cu[b + 1] - cu[b];
     const int p = static_cast<int>(t - cu[b]);
-    if (L > c.max_len || !c.valid[0]) continue;  // precondition violated: leave the slot alone
+    // precondition violated (a sequence past max_len, or cu_seqlens not
+    // non-decreasing): leave the slot alone
+    if (L > c.max_len || p < 0 || p >= L || !c.valid[0]) continue;
     const int64_t slot = static_cast<int64_t>(b) * c.Hkv + g;
     const int kb = p / kBlock;
     const int ring = c.ring[slot];
@@ -137,7 +139,12 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(CacheView c, const int3
     *reinterpret_cast<u32x4*>(c.V + dst) = *reinterpret_cast<const u32x4*>(V + src);
   }
   if (blockIdx.x == 0)
-    for (int b = threadIdx.x; b < c.B; b += blockDim.x) c.lengths[b] = cu[b + 1] - cu[b];
+    for (int b = threadIdx.x; b < c.B; b += blockDim.x) {
+      // a length outside [0, max_len] (contents that break the precondition)
+      // marks the sequence full, so that no decode step writes its slot
+      const int L = cu[b + 1] - cu[b];
+      c.lengths[b] = (L >= 0 && L <= c.max_len) ? L : c.max_len;
+    }
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attn_kernel(CacheView c
   const int pos = c.lengths[b];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, lg = lane / 16, li = lane % 16;
   const int64_t part0 = (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * a.G) * a.n_chunks;
-  const bool full = pos >= c.max_len || !c.valid[0];
+  const bool full = pos < 0 || pos >= c.max_len || !c.valid[0];
   const int qb = pos / kBlock;
   const int mode = c.mode[slot];
   const int w = sa_window(qb + 1, c.n_sink, c.window_blocks, c.keep_fraction);

@@ -72,7 +72,9 @@ template <typename E, int VEC>
 __global__ __launch_bounds__(256) void dual_merge_kernel(
     const int32_t* __restrict__ cu, int32_t B, const int8_t* __restrict__ modes, int32_t Hkv,
     int32_t G, int64_t T, int32_t Hq, int32_t d, const E* __restrict__ O_sa,
-    const float* __restrict__ lse_sa, E* O_fa, float* lse_fa, E* __restrict__ O) {
+    const float* __restrict__ lse_sa, E* O_fa, float* lse_fa, E* __restrict__ O,
+    const int32_t* __restrict__ meta, int32_t stamp) {
+  if (meta[kMetaStamp] != stamp) return;  // the planner rejected the device contents
   const int cpr = d / VEC;
   const int64_t total = T * Hq * cpr;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
@@ -203,19 +205,20 @@ hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float t
 
 hipError_t launch_dual_merge(const Shape& s, const int32_t* cu, const int8_t* modes,
                              const void* O_sa, const float* lse_sa, void* O_fa, float* lse_fa,
-                             void* O, hipStream_t st) {
+                             void* O, const int32_t* meta, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
+  const int32_t stamp = plan_stamp(s);
   const int vec = s.elem_bytes == 2 ? 8 : 4;  // 16-byte accesses
   const int64_t threads = s.T * s.Hq * (s.d / vec);
   const unsigned grid = static_cast<unsigned>(threads / 256 + 1 < 65536 ? threads / 256 + 1 : 65536);
   if (s.elem_bytes == 2)
     hipLaunchKernelGGL((dual_merge_kernel<__bf16, 8>), dim3(grid), dim3(256), 0, st, cu, s.B,
                        modes, s.Hkv, s.G, s.T, s.Hq, s.d, static_cast<const __bf16*>(O_sa), lse_sa,
-                       static_cast<__bf16*>(O_fa), lse_fa, static_cast<__bf16*>(O));
+                       static_cast<__bf16*>(O_fa), lse_fa, static_cast<__bf16*>(O), meta, stamp);
   else
     hipLaunchKernelGGL((dual_merge_kernel<float, 4>), dim3(grid), dim3(256), 0, st, cu, s.B,
                        modes, s.Hkv, s.G, s.T, s.Hq, s.d, static_cast<const float*>(O_sa), lse_sa,
-                       static_cast<float*>(O_fa), lse_fa, static_cast<float*>(O));
+                       static_cast<float*>(O_fa), lse_fa, static_cast<float*>(O), meta, stamp);
   return hipGetLastError();
 }
 

@@ -115,8 +115,25 @@ enum Meta : int {
   kMetaTiles = 0,       // sum over sequences of ceil(L_b / BMq); items = tiles * Hkv
   kMetaStamp = 1,       // plan_stamp() of the sizes the list was built for
   kMetaXaRows = 2,      // XA mode: number of (sequence, KV head) rows in XA mode
+  kMetaError = 3,       // MetaError bits of the device contents the planner found invalid
   kMetaSlots = 64
 };
+
+// Device-content checks of the planner (setup_kernel).  Any set bit makes the
+// planner write stamp 0 and zero tiles, so that no later kernel of the call
+// (XA selection, work list, attention, backward, merge) reads Q, K, V or
+// writes an output.
+enum MetaError : int32_t {
+  kErrCuStart = 1,      // cu_seqlens[0] != 0
+  kErrCuOrder = 2,      // cu_seqlens decreases somewhere
+  kErrCuEnd = 4,        // cu_seqlens[B] != total_tokens
+  kErrSeqLen = 8,       // a sequence is longer than max_seqlen
+  kErrMode = 16         // a mode value outside {0, 1}
+};
+
+// Upper bound the host accepts for n_sink_blocks and window_blocks, so that
+// block arithmetic on them (sums of a few blocks counts) stays in int32.
+constexpr int32_t kMaxGeomBlocks = 1 << 24;
 
 // Byte layout of the workspace, a pure function of the host-visible sizes.
 struct Workspace {
@@ -178,6 +195,13 @@ hipError_t launch_route(const void* K, bool bf16, const int32_t* cu, int32_t B, 
 
 hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,
                            const int32_t* cu, const Workspace& ws, char* base, hipStream_t st);
+// The two halves of launch_worklist: the per-sequence setup with its
+// device-content checks, then the items and their cost order (the XA
+// selection runs between the two).
+hipError_t launch_setup(const Shape& s, const Geometry& g, const int8_t* modes, const int32_t* cu,
+                        const Workspace& ws, char* base, hipStream_t st);
+hipError_t launch_items(const Shape& s, const Geometry& g, const int8_t* modes, const int32_t* cu,
+                        const Workspace& ws, char* base, hipStream_t st);
 
 // Outputs of an attention launch: items of mode FA or SA write O / lse,
 // items of the middle set O_mid / lse_mid (dual-mode forward only).
@@ -301,9 +325,10 @@ hipError_t launch_gumbel_route(const float* logits, const float* gumbel, float t
                                float* r_soft, int8_t* modes, hipStream_t st);
 // O_fa / lse_fa hold the middle-set partial on entry and the FA result on
 // exit; O (if not null) receives the straight-through mix selected by modes.
+// Does nothing unless meta holds the plan stamp of s.
 hipError_t launch_dual_merge(const Shape& s, const int32_t* cu, const int8_t* modes,
                              const void* O_sa, const float* lse_sa, void* O_fa, float* lse_fa,
-                             void* O, hipStream_t st);
+                             void* O, const int32_t* meta, hipStream_t st);
 
 // Matrix-core ceiling probe (ea_probe.hip) and its FLOP count.
 hipError_t launch_mfma_probe(float* out, int32_t n_workgroups, int32_t iters, uint32_t seed,

@@ -64,14 +64,30 @@ __device__ int32_t block_exclusive_scan(int32_t* a, int64_t n, int32_t* tmp /* [
   return carry;
 }
 
-// Per-sequence query tiles and sparse window.
+// Per-sequence query tiles and sparse window, after the device-content checks:
+// cu_seqlens starts at 0, never decreases and ends at T, no sequence is longer
+// than max_seqlen (buffers are sized from it), and every mode is 0 or 1.  On
+// a failed check the header gets the MetaError bits, zero tiles and stamp 0,
+// which every later kernel of the call takes as "do nothing".
 __global__ __launch_bounds__(kScanThreads) void setup_kernel(
-    const int32_t* __restrict__ cu, int32_t B, int32_t BMq, int32_t n_sink, int32_t window_blocks,
+    const int32_t* __restrict__ cu, const int8_t* __restrict__ modes, int32_t B, int32_t Hkv,
+    int64_t T, int32_t max_seqlen, int32_t BMq, int32_t n_sink, int32_t window_blocks,
     float keep_fraction, int32_t stamp, int32_t* __restrict__ meta,
     int32_t* __restrict__ tile_prefix, int32_t* __restrict__ seq_w) {
   __shared__ int32_t tmp[kScanThreads / 64 + 1];
+  __shared__ int32_t err;
+  if (threadIdx.x == 0) err = 0;
+  __syncthreads();
+  int32_t bad = 0;
+  if (threadIdx.x == 0) {
+    if (cu[0] != 0) bad |= kErrCuStart;
+    if (static_cast<int64_t>(cu[B]) != T) bad |= kErrCuEnd;
+  }
   for (int b = threadIdx.x; b < B; b += kScanThreads) {
-    const int L = max(0, cu[b + 1] - cu[b]);
+    const int64_t len = static_cast<int64_t>(cu[b + 1]) - cu[b];
+    if (len < 0) bad |= kErrCuOrder;
+    if (len > max_seqlen) bad |= kErrSeqLen;
+    const int L = len > 0 ? static_cast<int>(len) : 0;
     const int N = (L + kBlock - 1) / kBlock;
     tile_prefix[b] = (L + BMq - 1) / BMq;
     int w = window_blocks;
@@ -81,14 +97,24 @@ __global__ __launch_bounds__(kScanThreads) void setup_kernel(
       const int k = max(n_sink + 1, static_cast<int>(keep));
       w = k - n_sink;
     }
-    seq_w[b] = w;
+    // a window of N blocks already covers every causal key of the sequence;
+    // the clamp keeps sums such as (last key block + w) inside int32
+    seq_w[b] = min(w, max(N, 1));
   }
+  if (modes) {
+    const int64_t n = static_cast<int64_t>(B) * Hkv;
+    for (int64_t i = threadIdx.x; i < n; i += kScanThreads)
+      if (static_cast<uint8_t>(modes[i]) > 1u) bad |= kErrMode;
+  }
+  if (bad) atomicOr(&err, bad);
   __syncthreads();
   const int32_t tiles = block_exclusive_scan(tile_prefix, B, tmp);
   if (threadIdx.x == 0) {
-    tile_prefix[B] = tiles;
-    meta[kMetaTiles] = tiles;
-    meta[kMetaStamp] = stamp;
+    tile_prefix[B] = err ? 0 : tiles;
+    meta[kMetaTiles] = err ? 0 : tiles;
+    meta[kMetaXaRows] = 0;
+    meta[kMetaError] = err;
+    meta[kMetaStamp] = err ? 0 : stamp;
   }
 }
 
@@ -210,8 +236,20 @@ Workspace plan_workspace(const Shape& s) {
   return w;
 }
 
-hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,
-                           const int32_t* cu, const Workspace& ws, char* base, hipStream_t st) {
+hipError_t launch_setup(const Shape& s, const Geometry& g, const int8_t* modes, const int32_t* cu,
+                        const Workspace& ws, char* base, hipStream_t st) {
+  int32_t* meta = reinterpret_cast<int32_t*>(base + ws.meta);
+  int32_t* tile_prefix = reinterpret_cast<int32_t*>(base + ws.tile_prefix);
+  int32_t* seq_w = reinterpret_cast<int32_t*>(base + ws.seq_w);
+  // (modes may be null: the dual-mode forward without the mixed output)
+  hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(kScanThreads), 0, st, cu, modes, s.B,
+                     s.Hkv, s.T, s.max_seqlen, s.BMq, g.n_sink, g.window_blocks, g.keep_fraction,
+                     plan_stamp(s), meta, tile_prefix, seq_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_items(const Shape& s, const Geometry& g, const int8_t* modes, const int32_t* cu,
+                        const Workspace& ws, char* base, hipStream_t st) {
   int32_t* meta = reinterpret_cast<int32_t*>(base + ws.meta);
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(base + ws.tile_prefix);
   int32_t* seq_w = reinterpret_cast<int32_t*>(base + ws.seq_w);
@@ -220,8 +258,6 @@ hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* mode
   int32_t* vals_in = reinterpret_cast<int32_t*>(base + ws.vals_in);
   int32_t* order = reinterpret_cast<int32_t*>(base + ws.order);
   Item* raw = reinterpret_cast<Item*>(base + ws.items_raw);
-  hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(kScanThreads), 0, st, cu, s.B, s.BMq, g.n_sink,
-                     g.window_blocks, g.keep_fraction, plan_stamp(s), meta, tile_prefix, seq_w);
   const unsigned grid = static_cast<unsigned>((ws.max_items + 255) / 256);
   const int32_t* xa_cnt = s.xa ? reinterpret_cast<const int32_t*>(base + ws.xa_cnt) : nullptr;
   hipLaunchKernelGGL(items_kernel, dim3(grid), dim3(256), 0, st, cu, modes, s.B, s.Hkv, s.BMq,
@@ -233,6 +269,13 @@ hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* mode
   return hipcub::DeviceRadixSort::SortPairs(base + ws.sort_tmp, tmp_bytes, keys_in, keys_out,
                                             vals_in, order, static_cast<int>(ws.max_items), 0,
                                             key_bits(max_key(ws.nbins)), st);
+}
+
+hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,
+                           const int32_t* cu, const Workspace& ws, char* base, hipStream_t st) {
+  hipError_t e = launch_setup(s, g, modes, cu, ws, base, st);
+  if (e != hipSuccess) return e;
+  return launch_items(s, g, modes, cu, ws, base, st);
 }
 
 }  // namespace ea

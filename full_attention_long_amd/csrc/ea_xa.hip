@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kXaThreads) void xa_rows_kernel(const int8_t* __res
                                                               int32_t* __restrict__ meta) {
   __shared__ int32_t red[kXaWaves + 1];
   int32_t base = 0;
-  const int n = B * Hkv;
+  // invalid device contents (the planner's checks ran first): no XA row at all
+  const int n = meta[kMetaError] != 0 ? 0 : B * Hkv;
   for (int r0 = 0; r0 < n; r0 += kXaThreads) {
     const int r = r0 + static_cast<int>(threadIdx.x);
     const bool x = r < n && cu[r / Hkv + 1] > cu[r / Hkv] &&
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  if (i < 0 || static_cast<int64_t>(i) * kXaBlock >= L) return;
+  if (i < 0 || i >= a.nqb || static_cast<int64_t>(i) * kXaBlock >= L) return;
   const int ng = (L + S - 1) / S;  // position groups of the sequence
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;

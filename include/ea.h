@@ -34,8 +34,21 @@
  *    stream) and never synchronise the host.
  *  - Host-checkable errors return a negative status before anything is
  *    launched; ea_last_error() then returns a message (thread-local).  A
- *    failed launch returns EA_ERR_HIP.  Device contents (cu_seqlens values,
- *    mode values) are preconditions and are not read by the host.
+ *    failed launch returns EA_ERR_HIP.
+ *  - Device contents are checked on the device by the planner that every
+ *    prefill, dual, XA and backward call runs first: cu_seqlens[0] == 0,
+ *    cu_seqlens non-decreasing, cu_seqlens[B] == total_tokens, every length
+ *    <= max_seqlen, and every mode 0 or 1 (the router paragraph on Fig. 3(b)
+ *    of the paper body: the hard decision per KV head is 0 or 1).  On a
+ *    failed check the planner marks its workspace invalid and no later kernel
+ *    of the call reads Q, K, V or writes an output (the outputs keep their
+ *    previous contents).  By default nothing waits for the verdict:
+ *    ea_workspace_status() reads it.  With the environment variable
+ *    EA_VALIDATE set (to anything but "" or "0"), every such call waits for
+ *    the checks itself and returns EA_ERR_INVALID_ARG with a message naming
+ *    the failed check; ea_route and ea_kvcache_prefill then also copy
+ *    cu_seqlens to the host and check it there.
+ *  - n_sink_blocks and window_blocks are at most 2^24 (EA_ERR_INVALID_ARG).
  */
 #ifndef EA_H
 #define EA_H
@@ -47,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EA_ABI_VERSION 1
+#define EA_ABI_VERSION 2
 
 typedef enum {
   EA_OK = 0,
@@ -106,6 +119,19 @@ int32_t ea_abi_version(void);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ea_last_error(void);
+
+/* ea_workspace_status - verdict of the planner's device-content checks.
+ *
+ *   workspace        a workspace that a prefill, plan, dual, XA or backward
+ *                    call has planned (its header is read; the rest is not)
+ *   workspace_bytes  its size, at least 256
+ *   stream           the stream the planning call ran on
+ *
+ * Waits for `stream`, then returns EA_OK if the last plan written into the
+ * workspace passed every check listed in the conventions above, or
+ * EA_ERR_INVALID_ARG with a message naming the failed checks.  A workspace
+ * no call has planned holds no verdict (its result is meaningless). */
+ea_status ea_workspace_status(const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ea_route - hard FA/SA decision per (sequence, KV head).
  *

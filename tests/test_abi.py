@@ -23,11 +23,11 @@ def test_every_header_function_is_exported():
                           "ea_hybrid_backward_workspace_size", "ea_hybrid_backward",
                           "ea_router_logit_grad_workspace_size", "ea_router_logit_grad",
                           "ea_xa_prefill_workspace_size", "ea_xa_prefill",
-                          "ea_xa_prefill_plan", "ea_xa_prefill_run"}
+                          "ea_xa_prefill_plan", "ea_xa_prefill_run", "ea_workspace_status"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert ea.ea_abi_version() == 1
+    assert ea.ea_abi_version() == 2
 
 
 def test_workspace_size_bounds():
@@ -68,7 +68,9 @@ def _prefill(**kw):
     (dict(dtype=7), -2, "dtype"),
     (dict(block=128), -2, "block"),
     (dict(n_sink=-1), -1, "n_sink"),
+    (dict(n_sink=2**24 + 1), -1, "n_sink"),
     (dict(window=-2), -1, "window_blocks"),
+    (dict(window=2**31 - 1), -1, "window_blocks"),
     (dict(keep=0.0), -1, "keep_fraction"),
     (dict(keep=1.5), -1, "keep_fraction"),
     (dict(scale=-1.0), -1, "softmax_scale"),
@@ -342,3 +344,19 @@ def test_xa_prefill_host_errors():
                                None, A, None, A, 1 << 40, None) == -1
     assert L.ea_xa_prefill_run(A, A, None, 1, A, A, 1, 1000, 1000, 8, 2, 128, ctypes.byref(sp),
                                ctypes.byref(xp), A, None, A, 1 << 40, None) == -1
+
+
+def test_workspace_status_host_errors():
+    L = ea.lib()
+    assert L.ea_workspace_status(None, 4096, None) == bnd.EA_ERR_INVALID_ARG
+    assert "null pointer" in ea.ea_last_error()
+    assert L.ea_workspace_status(FAKE, 16, None) == bnd.EA_ERR_WORKSPACE
+    assert "at least" in ea.ea_last_error()
+
+
+def test_cache_desc_rejects_huge_geometry():
+    L = ea.lib()
+    for ns, wb in [(2**24 + 1, 0), (1, 2**31 - 1)]:
+        desc = bnd.KVCacheDesc(1, 8, 128, 4096, ns, wb, 0.2)
+        assert L.ea_kvcache_init(ctypes.byref(desc), FAKE, FAKE, 1 << 30, None) == bnd.EA_ERR_INVALID_ARG
+        assert "2^24" in ea.ea_last_error() or "16777216" in ea.ea_last_error()
