@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     ea_hybrid_backward_workspace_size,
     ea_hybrid_prefill,
     ea_hybrid_prefill_plan,
+    ea_hybrid_prefill_plan_layout,
     ea_hybrid_prefill_run,
     ea_hybrid_prefill_workspace_size,
     ea_last_error,

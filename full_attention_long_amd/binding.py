@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
     L.ea_hybrid_prefill.restype = i32
     L.ea_hybrid_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                     ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
+    L.ea_hybrid_prefill_plan_layout.restype = i32
+    L.ea_hybrid_prefill_plan_layout.argtypes = [i32, i64, i32, i32, i32, i32, i32,
+                                                ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.ea_hybrid_prefill_plan.restype = i32
     L.ea_hybrid_prefill_plan.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                          ctypes.POINTER(SparsityParams), vp, sz, vp]
@@ -315,6 +319,16 @@ def ea_hybrid_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: in
                                    B, T, max_seqlen, Hq, Hkv, d, ctypes.byref(sp), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def ea_hybrid_prefill_plan_layout(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype_code):
+    """Byte offsets of the item records, sort keys and list order inside a
+    planned workspace, and the number of list slots (a dict)."""
+    out = [ctypes.c_int64(0) for _ in range(4)]
+    _check(lib().ea_hybrid_prefill_plan_layout(B, total_tokens, max_seqlen, Hq, Hkv, head_dim,
+                                               dtype_code, *[ctypes.byref(o) for o in out]))
+    return {"items": out[0].value, "keys": out[1].value, "order": out[2].value,
+            "n_slots": out[3].value}
 
 
 def ea_hybrid_prefill_plan(modes, cu_seqlens, total_tokens: int, max_seqlen: int, Hq: int, Hkv: int,

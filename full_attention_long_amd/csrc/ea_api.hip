@@ -222,6 +222,23 @@ size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t
   return ea::plan_workspace(s).total;
 }
 
+ea_status ea_hybrid_prefill_plan_layout(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                        int32_t Hq, int32_t Hkv, int32_t head_dim, ea_dtype dtype,
+                                        int64_t* items_offset, int64_t* keys_offset,
+                                        int64_t* order_offset, int64_t* n_slots) {
+  ea::Shape s;
+  ea_status st = check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s);
+  if (st != EA_OK) return st;
+  if (!items_offset || !keys_offset || !order_offset || !n_slots)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  const ea::Workspace ws = ea::plan_workspace(s);
+  *items_offset = static_cast<int64_t>(ws.items_raw);
+  *keys_offset = static_cast<int64_t>(ws.keys);
+  *order_offset = static_cast<int64_t>(ws.order);
+  *n_slots = ws.max_items;
+  return ok();
+}
+
 ea_status ea_hybrid_prefill_plan(const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
                                  int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
                                  int32_t Hkv, int32_t head_dim, ea_dtype dtype,

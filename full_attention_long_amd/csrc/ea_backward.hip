@@ -23,7 +23,6 @@
 
 #include <math.h>
 
-#include <hipcub/hipcub.hpp>
 
 namespace ea {
 namespace {
@@ -501,19 +500,16 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
 // Cost (query blocks walked) of every dK/dV item, as a sort key: most
 // expensive first in bands of 2^kCostBandShift blocks, empty items last.
 __global__ __launch_bounds__(256) void dkv_items_kernel(BwdArgs a, int32_t maxcost,
-                                                        uint32_t* __restrict__ keys,
-                                                        int32_t* __restrict__ vals) {
+                                                        uint32_t* __restrict__ keys) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (x >= a.dkv_n) return;
-  vals[x] = static_cast<int32_t>(x);
   const int pair = static_cast<int>(x % a.npair);
   const int64_t rest = x / a.npair;
   const int g = static_cast<int>(rest % a.Hkv);
   const int b = static_cast<int>(rest / a.Hkv);
   const int L = a.cu[b + 1] - a.cu[b];
-  const uint32_t last = static_cast<uint32_t>(maxcost >> kCostBandShift) + 1;
   if (a.meta[kMetaStamp] != a.stamp || pair * kDkvKeys >= L) {
-    keys[x] = last;
+    keys[x] = empty_key(maxcost);
     return;
   }
   const int N = (L + kBlock - 1) / kBlock;
@@ -522,13 +518,7 @@ __global__ __launch_bounds__(256) void dkv_items_kernel(BwdArgs a, int32_t maxco
   const bool sa = a.modes[static_cast<int64_t>(b) * a.Hkv + g] != 0;
   const int qb_hi = (sa && kb0 >= a.n_sink) ? min(N - 1, kb1 + a.seq_w[b] - 1) : N - 1;
   const int cost = qb_hi - kb0 + 1;
-  keys[x] = static_cast<uint32_t>((maxcost - min(cost, maxcost)) >> kCostBandShift);
-}
-
-int bits_for(uint32_t max_value) {
-  int bits = 1;
-  while ((int64_t(1) << bits) <= max_value) ++bits;
-  return bits;
+  keys[x] = cost_key(cost, maxcost);
 }
 
 }  // namespace
@@ -539,39 +529,23 @@ DkvList dkv_list_layout(const Shape& s) {
   l.npair = static_cast<int32_t>((static_cast<int64_t>(s.max_seqlen) + kDkvKeys - 1) / kDkvKeys);
   l.n = static_cast<int64_t>(s.B) * s.Hkv * l.npair;
   l.maxcost = (s.max_seqlen + kBlock - 1) / kBlock;
-  size_t tmp = 0;
-  if (hipcub::DeviceRadixSort::SortPairs(
-          nullptr, tmp, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
-          static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr), static_cast<int>(l.n), 0,
-          bits_for(static_cast<uint32_t>(l.maxcost >> kCostBandShift) + 1),
-          static_cast<hipStream_t>(nullptr)) != hipSuccess)
-    tmp = 0;
   size_t off = 0;
-  l.keys_in = off;  off = align(off + sizeof(uint32_t) * l.n);
-  l.keys_out = off; off = align(off + sizeof(uint32_t) * l.n);
-  l.vals_in = off;  off = align(off + sizeof(int32_t) * l.n);
-  l.order = off;    off = align(off + sizeof(int32_t) * l.n);
-  l.sort_tmp = off; off = align(off + tmp);
-  l.sort_tmp_bytes = tmp;
+  l.keys = off;  off = align(off + sizeof(uint32_t) * l.n);
+  l.order = off; off = align(off + sizeof(int32_t) * l.n);
   l.total = off;
   return l;
 }
 
 hipError_t launch_backward(const Shape& s, const Geometry& g, BwdArgs args, const DkvList& l,
                            char* list_base, hipStream_t st) {
-  uint32_t* keys_in = reinterpret_cast<uint32_t*>(list_base + l.keys_in);
-  uint32_t* keys_out = reinterpret_cast<uint32_t*>(list_base + l.keys_out);
-  int32_t* vals_in = reinterpret_cast<int32_t*>(list_base + l.vals_in);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(list_base + l.keys);
   int32_t* order = reinterpret_cast<int32_t*>(list_base + l.order);
   args.dkv_order = order;
   args.dkv_n = l.n;
   args.npair = l.npair;
   hipLaunchKernelGGL(dkv_items_kernel, dim3(static_cast<unsigned>((l.n + 255) / 256)), dim3(256), 0,
-                     st, args, l.maxcost, keys_in, vals_in);
-  size_t tmp_bytes = l.sort_tmp_bytes;
-  hipError_t e0 = hipcub::DeviceRadixSort::SortPairs(
-      list_base + l.sort_tmp, tmp_bytes, keys_in, keys_out, vals_in, order, static_cast<int>(l.n), 0,
-      bits_for(static_cast<uint32_t>(l.maxcost >> kCostBandShift) + 1), st);
+                     st, args, l.maxcost, keys);
+  hipError_t e0 = launch_key_sort(keys, l.n, order, st);
   if (e0 != hipSuccess) return e0;
   const int64_t dkv_items = l.n;
   const int64_t rows = s.T * s.Hq * (s.d / 8);

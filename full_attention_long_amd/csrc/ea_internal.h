@@ -24,6 +24,26 @@ constexpr int kNumXcd = 8;
 constexpr int kCostBandShift = 5;
 // Key/value block of the sparse pattern and of the attention inner loop.
 constexpr int kBlock = 64;
+// Bins of the work lists' counting sort (one workgroup; its per-wave
+// histograms take kSortWaves * kSortBands * 4 bytes of LDS).
+constexpr int kSortBands = 1024;
+constexpr int kSortWaves = 16;
+
+// Sort key of a work item of `cost` (visible key blocks, or query blocks
+// walked) when no item costs more than maxcost: 0 for the costliest band of
+// 2^kCostBandShift blocks, growing as the cost falls; capped below
+// kSortBands - 1 (only lists of sequences beyond two million tokens have more
+// bands, and then their cheapest bands share the last bin).
+__host__ __device__ inline uint32_t cost_key(int cost, int maxcost) {
+  const int c = cost < maxcost ? cost : maxcost;
+  const int k = (maxcost - c) >> kCostBandShift;
+  return static_cast<uint32_t>(k < kSortBands - 2 ? k : kSortBands - 2);
+}
+// Sort key of the list's empty slots: after every real item.
+__host__ __device__ inline uint32_t empty_key(int maxcost) {
+  const int k = (maxcost >> kCostBandShift) + 1;
+  return static_cast<uint32_t>(k < kSortBands - 1 ? k : kSortBands - 1);
+}
 
 // Key-block sets an attention work item can cover.
 enum ItemMode : int32_t {
@@ -137,8 +157,8 @@ constexpr int32_t kMaxGeomBlocks = 1 << 24;
 
 // Byte layout of the workspace, a pure function of the host-visible sizes.
 struct Workspace {
-  size_t meta, tile_prefix, seq_w, keys_in, keys_out, vals_in, order, items_raw, sort_tmp;
-  size_t sort_tmp_bytes, total;
+  size_t meta, tile_prefix, seq_w, keys, order, items_raw;
+  size_t total;
   int64_t max_items;   // bound on work items
   int32_t nbins;       // cost bins of the sort key
   // XA mode only (Shape.xa): per (sequence, KV head, query block) the number
@@ -202,6 +222,11 @@ hipError_t launch_setup(const Shape& s, const Geometry& g, const int8_t* modes, 
                         const Workspace& ws, char* base, hipStream_t st);
 hipError_t launch_items(const Shape& s, const Geometry& g, const int8_t* modes, const int32_t* cu,
                         const Workspace& ws, char* base, hipStream_t st);
+
+// Stable counting sort of n entries by key (each key < kSortBands): order
+// receives the entry indices 0..n-1, ascending by key and, within a key, by
+// index.  One workgroup; stream-ordered.
+hipError_t launch_key_sort(const uint32_t* keys, int64_t n, int32_t* order, hipStream_t st);
 
 // Outputs of an attention launch: items of mode FA or SA write O / lse,
 // items of the middle set O_mid / lse_mid (dual-mode forward only).
@@ -304,7 +329,7 @@ constexpr int kDkvKeys = 32 * kDkvWaves;
 // Cost-ordered list of the dK/dV kernel's items (sequence, KV head, key
 // group), in its own workspace region.
 struct DkvList {
-  size_t keys_in, keys_out, vals_in, order, sort_tmp, sort_tmp_bytes, total;
+  size_t keys, order, total;
   int64_t n;
   int32_t npair, maxcost;
 };

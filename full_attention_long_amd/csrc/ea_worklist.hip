@@ -11,7 +11,7 @@
 // its head's SA set and once over the causal blocks outside it, whose partial
 // results the merge kernel combines into the FA output (ea_dual.hip).
 //
-// Items are sorted by descending cost with a stable radix sort over the raw
+// Items are sorted by descending cost with a stable counting sort over the raw
 // order (KV head, sequence, query tile), so the list is longest-processing-
 // time first, items of equal cost stay in query order within a head, and the
 // whole layer, FA and SA tiles together, runs as one launch without splitting
@@ -24,8 +24,6 @@
 #include "ea_internal.h"
 
 #include <math.h>
-
-#include <hipcub/hipcub.hpp>
 
 namespace ea {
 namespace {
@@ -128,15 +126,9 @@ __device__ __forceinline__ int find_seq(const int32_t* prefix, int B, int32_t x)
   return lo;
 }
 
-// Sort key of a cost: 0 for the most expensive band of 2^kCostBandShift
-// blocks; max_key(nbins) for the unused slots past the item count.
-__host__ __device__ __forceinline__ uint32_t max_key(int32_t nbins) {
-  return static_cast<uint32_t>(((nbins - 1) >> kCostBandShift) + 1);
-}
-
 // Raw item x (part major, then KV head, sequence, and query tile from the
-// last, most expensive tile down), its banded sort key and its index as the
-// sort value; the stable sort keeps this raw order inside a band.  With one
+// last, most expensive tile down) and its banded sort key; the stable sort
+// keeps this raw order inside a band.  With one
 // part an item covers its head's routed mode; with two (dual-mode forward)
 // part 0 covers every head's SA set and part 1 the rest of its causal blocks.
 __global__ __launch_bounds__(256) void items_kernel(
@@ -144,15 +136,13 @@ __global__ __launch_bounds__(256) void items_kernel(
     int32_t BMq, int32_t parts, int32_t head_config, int32_t n_sink,
     const int32_t* __restrict__ meta, const int32_t* __restrict__ tile_prefix,
     const int32_t* __restrict__ seq_w, const int32_t* __restrict__ xa_cnt, int32_t xa_nqb,
-    int32_t nbins, int64_t max_items, Item* __restrict__ raw, uint32_t* __restrict__ keys,
-    int32_t* __restrict__ vals) {
+    int32_t maxcost, int64_t max_items, Item* __restrict__ raw, uint32_t* __restrict__ keys) {
   const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (x >= max_items) return;
-  vals[x] = static_cast<int32_t>(x);
   const int32_t tiles = meta[kMetaTiles];
   const int64_t per_part = static_cast<int64_t>(tiles) * Hkv;
   if (x >= per_part * parts) {
-    keys[x] = max_key(nbins);
+    keys[x] = empty_key(maxcost);
     return;
   }
   const int part = static_cast<int>(x / per_part);
@@ -183,13 +173,80 @@ __global__ __launch_bounds__(256) void items_kernel(
   it.cost = cost;
   it.mode = mode;
   raw[x] = it;
-  keys[x] = static_cast<uint32_t>((nbins - 1 - min(cost, nbins - 1)) >> kCostBandShift);
+  keys[x] = cost_key(cost, maxcost);
 }
 
-int key_bits(uint32_t max_value) {
-  int bits = 1;
-  while ((int64_t(1) << bits) <= max_value) ++bits;
-  return bits;
+// Stable counting sort by key, one workgroup of kSortWaves waves.  The n
+// entries split into kSortWaves consecutive segments, one per wave:
+//  1. each wave counts its segment's keys into its own LDS histogram;
+//  2. an exclusive scan in (key, wave) order turns the histograms into the
+//     first output slot of each (key, wave) run;
+//  3. each wave walks its segment in steps of 64 entries; a lane's rank
+//     among the equal keys of its step (lanes below it with the same key)
+//     gives its slot, and the last lane of each key advances that key's slot.
+// Equal keys thus keep their index order: within a step by lane, across steps
+// by the walk, across segments by the scan order.
+__global__ __launch_bounds__(kSortWaves * 64) void key_sort_kernel(const uint32_t* __restrict__ keys,
+                                                                   int64_t n,
+                                                                   int32_t* __restrict__ order) {
+  __shared__ int32_t hist[kSortWaves][kSortBands];
+  __shared__ int32_t tmp[kSortWaves + 1];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  for (int i = tid; i < kSortWaves * kSortBands; i += kSortWaves * 64) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t per = (n + kSortWaves - 1) / kSortWaves;
+  const int64_t seg0 = min(n, per * wave), seg1 = min(n, seg0 + per);
+  for (int64_t i = seg0 + lane; i < seg1; i += 64) atomicAdd(&hist[wave][min(keys[i], kSortBands - 1u)], 1);
+  __syncthreads();
+  // thread t owns key t (kSortBands == kSortWaves * 64): its total over the
+  // waves, scanned across keys, then split back over the waves
+  static_assert(kSortBands == kSortWaves * 64, "one key per thread in the scan");
+  int32_t tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) tot += hist[w][tid];
+  int32_t x = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < kSortWaves; ++w) {
+      const int32_t t = tmp[w];
+      tmp[w] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  int32_t slot = tmp[wave] + x - tot;
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) {
+    const int32_t c = hist[w][tid];
+    hist[w][tid] = slot;
+    slot += c;
+  }
+  __syncthreads();
+  for (int64_t base = seg0; base < seg1; base += 64) {
+    const int64_t i = base + lane;
+    const bool valid = i < seg1;
+    const uint32_t k = valid ? min(keys[i], kSortBands - 1u) : 0xFFFFFFFFu;
+    uint64_t same = 0;
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t kj = __builtin_amdgcn_readlane(k, j);
+      same |= static_cast<uint64_t>(kj == k) << j;
+    }
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    const int rank = __popcll(same & below);
+    const int32_t first = valid ? hist[wave][k] : 0;
+    if (valid) order[first + rank] = static_cast<int32_t>(i);
+    // every lane has read its key's slot before the run's last lane moves it
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (same >> lane) == 1u) hist[wave][k] = first + __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 }  // namespace
@@ -199,23 +256,13 @@ Workspace plan_workspace(const Shape& s) {
   Workspace w{};
   w.nbins = (s.max_seqlen + kBlock - 1) / kBlock + 1;
   w.max_items = static_cast<int64_t>(s.parts) * s.Hkv * ((s.T + s.BMq - 1) / s.BMq + s.B);
-  size_t sort_tmp = 0;
-  hipError_t e = hipcub::DeviceRadixSort::SortPairs(
-      nullptr, sort_tmp, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
-      static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
-      static_cast<int>(w.max_items), 0, key_bits(max_key(w.nbins)), static_cast<hipStream_t>(nullptr));
-  if (e != hipSuccess) sort_tmp = 0;
   size_t off = 0;
   w.meta = off;        off = align(off + sizeof(int32_t) * kMetaSlots);
   w.tile_prefix = off; off = align(off + sizeof(int32_t) * (s.B + 1));
   w.seq_w = off;       off = align(off + sizeof(int32_t) * s.B);
-  w.keys_in = off;     off = align(off + sizeof(uint32_t) * w.max_items);
-  w.keys_out = off;    off = align(off + sizeof(uint32_t) * w.max_items);
-  w.vals_in = off;     off = align(off + sizeof(int32_t) * w.max_items);
+  w.keys = off;        off = align(off + sizeof(uint32_t) * w.max_items);
   w.order = off;       off = align(off + sizeof(int32_t) * w.max_items);
   w.items_raw = off;   off = align(off + sizeof(Item) * w.max_items);
-  w.sort_tmp = off;    off = align(off + sort_tmp);
-  w.sort_tmp_bytes = sort_tmp;
   w.xa_nqb = (s.max_seqlen + kXaBlock - 1) / kXaBlock;
   w.xa_cnt = off;
   w.xa_list = off;
@@ -253,22 +300,22 @@ hipError_t launch_items(const Shape& s, const Geometry& g, const int8_t* modes, 
   int32_t* meta = reinterpret_cast<int32_t*>(base + ws.meta);
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(base + ws.tile_prefix);
   int32_t* seq_w = reinterpret_cast<int32_t*>(base + ws.seq_w);
-  uint32_t* keys_in = reinterpret_cast<uint32_t*>(base + ws.keys_in);
-  uint32_t* keys_out = reinterpret_cast<uint32_t*>(base + ws.keys_out);
-  int32_t* vals_in = reinterpret_cast<int32_t*>(base + ws.vals_in);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(base + ws.keys);
   int32_t* order = reinterpret_cast<int32_t*>(base + ws.order);
   Item* raw = reinterpret_cast<Item*>(base + ws.items_raw);
   const unsigned grid = static_cast<unsigned>((ws.max_items + 255) / 256);
   const int32_t* xa_cnt = s.xa ? reinterpret_cast<const int32_t*>(base + ws.xa_cnt) : nullptr;
   hipLaunchKernelGGL(items_kernel, dim3(grid), dim3(256), 0, st, cu, modes, s.B, s.Hkv, s.BMq,
                      s.parts, s.head_config, g.n_sink, meta, tile_prefix, seq_w, xa_cnt,
-                     ws.xa_nqb, ws.nbins, ws.max_items, raw, keys_in, vals_in);
+                     ws.xa_nqb, ws.nbins - 1, ws.max_items, raw, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  size_t tmp_bytes = ws.sort_tmp_bytes;
-  return hipcub::DeviceRadixSort::SortPairs(base + ws.sort_tmp, tmp_bytes, keys_in, keys_out,
-                                            vals_in, order, static_cast<int>(ws.max_items), 0,
-                                            key_bits(max_key(ws.nbins)), st);
+  return launch_key_sort(keys, ws.max_items, order, st);
+}
+
+hipError_t launch_key_sort(const uint32_t* keys, int64_t n, int32_t* order, hipStream_t st) {
+  hipLaunchKernelGGL(key_sort_kernel, dim3(1), dim3(kSortWaves * 64), 0, st, keys, n, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_worklist(const Shape& s, const Geometry& g, const int8_t* modes,

@@ -157,6 +157,21 @@ size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t
                                         int32_t Hq, int32_t Hkv, int32_t head_dim,
                                         ea_dtype dtype);
 
+/* ea_hybrid_prefill_plan_layout - where ea_hybrid_prefill_plan (and the
+ * one-shot call) put the work list inside a workspace of these sizes, for
+ * inspection.  Byte offsets of: the item records (n_slots records of five
+ * int32: sequence, KV head, query tile, cost in visible 64-key blocks,
+ * computation mode), their uint32 sort keys (0 = costliest band of 32 key
+ * blocks), and the int32 list order (record indices, ascending key, equal
+ * keys in record order).  The first tiles * Hkv slots are real items, tiles =
+ * int32 word 0 of the workspace; the rest are empty and sort last.  The
+ * layout is a pure function of the sizes (EA_OK, or EA_ERR_INVALID_ARG /
+ * EA_ERR_UNSUPPORTED for sizes the workspace query rejects). */
+ea_status ea_hybrid_prefill_plan_layout(int32_t B, int64_t total_tokens, int32_t max_seqlen,
+                                        int32_t Hq, int32_t Hkv, int32_t head_dim, ea_dtype dtype,
+                                        int64_t* items_offset, int64_t* keys_offset,
+                                        int64_t* order_offset, int64_t* n_slots);
+
 /* ea_hybrid_prefill - fused hybrid GQA attention forward over all heads.
  *
  *   Q           [T, Hq, head_dim]  of `dtype` (16-byte aligned)

@@ -23,7 +23,8 @@ def test_every_header_function_is_exported():
                           "ea_hybrid_backward_workspace_size", "ea_hybrid_backward",
                           "ea_router_logit_grad_workspace_size", "ea_router_logit_grad",
                           "ea_xa_prefill_workspace_size", "ea_xa_prefill",
-                          "ea_xa_prefill_plan", "ea_xa_prefill_run", "ea_workspace_status"}
+                          "ea_xa_prefill_plan", "ea_xa_prefill_run", "ea_workspace_status",
+                          "ea_hybrid_prefill_plan_layout"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -33,7 +34,7 @@ def test_every_header_function_is_exported():
 def test_workspace_size_bounds():
     ws = ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
     items = 8 * (131072 // 64 + 1)            # query tiles of 64 positions x 4 heads
-    per_item = 16 + 4 * 4                     # item record + sort keys and values in/out
+    per_item = 20 + 4 + 4                     # item record + sort key + sorted order
     assert items * per_item <= ws <= items * per_item + 4 * 2**20
     # no copy of K, V or Q: the workspace does not grow with head_dim or dtype
     assert ea.ea_hybrid_prefill_workspace_size(1, 1000, 1000, 32, 8, 128, bnd.EA_F32) == \
@@ -189,7 +190,7 @@ def test_dual_workspace_holds_two_entries_per_tile():
     one = ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
     two = ea.ea_dual_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, bnd.EA_BF16)
     items = 8 * (131072 // 64 + 1)
-    assert two - one >= items * (20 + 16) - 4096
+    assert two - one >= items * (20 + 8) - 4096
     assert ea.ea_dual_prefill_workspace_size(1, 1000, 1000, 30, 8, 128, 1) == 0
 
 
@@ -360,3 +361,16 @@ def test_cache_desc_rejects_huge_geometry():
         desc = bnd.KVCacheDesc(1, 8, 128, 4096, ns, wb, 0.2)
         assert L.ea_kvcache_init(ctypes.byref(desc), FAKE, FAKE, 1 << 30, None) == bnd.EA_ERR_INVALID_ARG
         assert "2^24" in ea.ea_last_error() or "16777216" in ea.ea_last_error()
+
+
+def test_plan_layout_is_inside_the_workspace():
+    for args in [(1, 131072, 131072, 32, 8, 128, 1), (3, 5000, 4000, 8, 2, 64, 0)]:
+        lay = ea.ea_hybrid_prefill_plan_layout(*args)
+        ws = ea.ea_hybrid_prefill_workspace_size(*args)
+        n = lay["n_slots"]
+        assert lay["items"] + 20 * n <= ws and lay["keys"] + 4 * n <= ws and lay["order"] + 4 * n <= ws
+        spans = sorted([(lay["items"], 20 * n), (lay["keys"], 4 * n), (lay["order"], 4 * n)])
+        assert all(a + la <= b for (a, la), (b, _) in zip(spans, spans[1:]))
+        assert spans[0][0] >= 256          # after the header
+    with pytest.raises(ea.EAError):
+        ea.ea_hybrid_prefill_plan_layout(0, 10, 10, 8, 2, 64, 1)
