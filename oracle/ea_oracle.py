@@ -310,6 +310,82 @@ def hybrid_attention_backward(Q, K, V, dO, modes, cu_seqlens, *, block=64, n_sin
     return dQ, dK, dV
 
 
+def _row_grad_stats(q, do, pos, Kseq, Vseq, mode, n_sink, w, block, scale):
+    """For query rows ``q``/``do`` [n, d] at sequence positions ``pos``, over
+    their whole visible key set: the probabilities P [n, jmax], dP = dO V^T
+    and D = rowsum(P * dP) (= rowsum(dO * O)); float64, two-pass softmax."""
+    jmax = int(pos.max()) + 1
+    Kc = np.asarray(Kseq[:jmax], np.float64)
+    Vc = np.asarray(Vseq[:jmax], np.float64)
+    s = (np.asarray(q, np.float64) @ Kc.T) * scale
+    mask = visible(pos[:, None], np.arange(jmax)[None, :], mode, n_sink, w, block)
+    s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = np.asarray(do, np.float64) @ Vc.T
+    D = (p * dp).sum(axis=1, keepdims=True)
+    return p, dp, D
+
+
+def hybrid_attention_backward_rows(Q, K, V, dO, modes, cu_seqlens, q_tokens, k_tokens, *,
+                                   block=64, n_sink=1, window_blocks=0, keep_fraction=0.2,
+                                   softmax_scale=0.0, chunk=64):
+    """hybrid_attention_backward at selected rows only.
+
+    dQ at the global token indices ``q_tokens`` (every query head), and dK, dV
+    at the global token indices ``k_tokens`` (every KV head).  Same chain rule:
+    for a query row i, dQ_i = scale sum_j P_ij (dP_ij - D_i) k_j over its
+    visible keys; for a key j of KV head g, dV_j = sum over the group's query
+    heads and the rows i that see j of P_ij dO_i, and dK_j = scale sum of
+    P_ij (dP_ij - D_i) q_i.  Each row's P and D come from its full visible
+    key set, so the cost is that of the rows involved.  Returns (dQ
+    [len(q_tokens), Hq, d], dK, dV [len(k_tokens), Hkv, d]), float64."""
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    scale = _scale(d, softmax_scale)
+    cu = np.asarray(cu_seqlens, np.int64)
+    q_tokens = np.asarray(q_tokens, np.int64)
+    k_tokens = np.asarray(k_tokens, np.int64)
+    dQ = np.zeros((len(q_tokens), Hq, d), dtype=np.float64)
+    dK = np.zeros((len(k_tokens), Hkv, d), dtype=np.float64)
+    dV = np.zeros((len(k_tokens), Hkv, d), dtype=np.float64)
+    qseg = np.searchsorted(cu, q_tokens, side="right") - 1
+    kseg = np.searchsorted(cu, k_tokens, side="right") - 1
+    for b in np.unique(np.concatenate([qseg, kseg])):
+        s0, e0 = int(cu[b]), int(cu[b + 1])
+        L = e0 - s0
+        ns, w = sa_geometry(L, block, n_sink, window_blocks, keep_fraction)
+        qsel = np.nonzero(qseg == b)[0]
+        ksel = np.nonzero(kseg == b)[0]
+        kpos = k_tokens[ksel] - s0
+        for hq in range(Hq):
+            g = hq // G
+            mode = int(modes[b, g])
+            Kb, Vb = K[s0:e0, g], V[s0:e0, g]
+            if len(qsel):
+                pos = q_tokens[qsel] - s0
+                p, dp, D = _row_grad_stats(Q[q_tokens[qsel], hq], dO[q_tokens[qsel], hq], pos, Kb,
+                                           Vb, mode, ns, w, block, scale)
+                dQ[qsel, hq] = scale * ((p * (dp - D)) @ np.asarray(Kb[:p.shape[1]], np.float64))
+            if len(ksel):
+                # rows that see at least one selected key
+                i_all = np.arange(int(kpos.min()), L)
+                sees = visible(i_all[:, None], kpos[None, :], mode, ns, w, block).any(axis=1)
+                rows = i_all[sees]
+                for r0 in range(0, len(rows), chunk):
+                    pos = rows[r0:r0 + chunk]
+                    p, dp, D = _row_grad_stats(Q[s0 + pos, hq], dO[s0 + pos, hq], pos, Kb, Vb, mode,
+                                               ns, w, block, scale)
+                    cols = np.minimum(kpos, p.shape[1] - 1)
+                    inside = kpos < p.shape[1]
+                    pk = np.where(inside[None, :], p[:, cols], 0.0)          # [rows, keys]
+                    dsk = pk * (np.where(inside[None, :], dp[:, cols], 0.0) - D)
+                    dV[ksel, g] += pk.T @ np.asarray(dO[s0 + pos, hq], np.float64)
+                    dK[ksel, g] += scale * (dsk.T @ np.asarray(Q[s0 + pos, hq], np.float64))
+    return dQ, dK, dV
+
+
 # ----------------------------------------------------------------------------
 # Decode: one new token per sequence
 # ----------------------------------------------------------------------------

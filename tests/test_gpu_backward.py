@@ -79,3 +79,50 @@ def test_backward_bitwise_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["qwen4b_s128k_sa2"])
+def test_backward_full_size_sampled(name):
+    """The 128K layer the backward is benchmarked on: dQ at sampled rows of
+    every query head of one FA and one SA KV group (rows at the start, the
+    middle and the end, where dQ sums over up to 131K keys), and dK, dV at
+    keys in the last three 64-key blocks of both groups (each summed over the
+    rows that see it, across the group's four query heads).  The oracle forms
+    its own P, dP and D for every row involved (hybrid_attention_backward_rows,
+    pinned to autograd on small cases)."""
+    from workloads.configs import WORKLOADS
+    wl = WORKLOADS[name]
+    note(f"backward full size {name}: generating")
+    c = gen.build_case(wl)
+    modes = np.asarray(c.target_modes, np.int8)
+    L, G = c.T, c.Hq // c.Hkv
+    dob = gen._draw_rows(901, 31, c.T, (c.Hq, c.d), 1.0, "bf16")
+    dv = to_device(c)
+    m = torch.from_numpy(modes).cuda()
+    geom = dict(n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+    note(f"backward full size {name}: forward and backward on the GPU, T={c.T}")
+    O, lse = ea.ea_hybrid_prefill(dv["q"], dv["k"], dv["v"], m, dv["cu"], L, **geom)
+    dO = dev_tensor(dob, "bf16")
+    dQ, dK, dV = ea.ea_hybrid_backward(dv["q"], dv["k"], dv["v"], O, dO, lse, m, dv["cu"], L, **geom)
+    torch.cuda.synchronize()
+    del dv, O, lse, dO
+    rng = np.random.default_rng(21)
+    qt = np.unique(np.concatenate([[0, 63, 64, 4000, L // 2 + 17, L - 65, L - 64, L - 1],
+                                   rng.integers(0, L, size=8)]))
+    kt = np.unique(np.concatenate([[L - 192, L - 129, L - 128, L - 65, L - 64, L - 1],
+                                   rng.integers(L - 192, L, size=6)]))
+    groups = [int(np.nonzero(modes[0] == 0)[0][0]), int(np.nonzero(modes[0] == 1)[0][0])]
+    qf, kf, vf = c.q_f32(), c.k_f32(), c.v_f32()
+    dof = gen.bf16_bits_to_f32(dob)
+    tq, tk = torch.from_numpy(qt).cuda(), torch.from_numpy(kt).cuda()
+    for g in groups:
+        hs = list(range(g * G, (g + 1) * G))
+        note(f"backward full size {name}: oracle for KV group {g} (mode {modes[0, g]}), "
+             f"{len(qt)} query rows, {len(kt)} keys")
+        ref_dq, ref_dk, ref_dv = orc.hybrid_attention_backward_rows(
+            np.ascontiguousarray(qf[:, hs]), np.ascontiguousarray(kf[:, [g]]),
+            np.ascontiguousarray(vf[:, [g]]), np.ascontiguousarray(dof[:, hs]), modes[:, [g]],
+            c.cu_seqlens, qt, kt, **geom)
+        compare_grad(dQ[tq][:, hs], ref_dq, f"dQ group {g}")
+        compare_grad(dK[tk][:, [g]], ref_dk, f"dK group {g}")
+        compare_grad(dV[tk][:, [g]], ref_dv, f"dV group {g}")

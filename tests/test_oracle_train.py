@@ -233,6 +233,35 @@ def test_backward_matches_autograd():
             np.testing.assert_allclose(a, r, rtol=0, atol=1e-11)
 
 
+def test_backward_rows_match_autograd_at_selected_rows():
+    # the sampled-row backward against torch autograd of the masked-softmax
+    # forward: ragged lengths, an empty sequence, FA and SA heads, sinks,
+    # keys near a sequence end (few rows see them) and at its start (all do)
+    lengths = [150, 0, 333, 64]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    Hq, Hkv, d = 4, 2, 16
+    Q, K, V, dO = _rand(140, T, Hq, d), _rand(141, T, Hkv, d), _rand(142, T, Hkv, d), _rand(143, T, Hq, d)
+    modes = np.array([[0, 1], [1, 0], [1, 1], [0, 1]], np.int8)
+    qt = np.array([0, 5, 149, 150, 200, 482, 483, 546])
+    kt = np.array([0, 63, 64, 149, 150, 151, 300, 482, 483, 500, 546])
+    for geom in (dict(n_sink=1, window_blocks=2), dict(n_sink=0, window_blocks=1),
+                 dict(n_sink=1, keep_fraction=0.3)):
+        dq, dk, dv = orc.hybrid_attention_backward_rows(Q, K, V, dO, modes, cu, qt, kt, chunk=37,
+                                                        **geom)
+        ref = _torch_grads(Q, K, V, dO, modes, cu, geom)
+        np.testing.assert_allclose(dq, ref[0][qt], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dk, ref[1][kt], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dv, ref[2][kt], rtol=0, atol=1e-11)
+    # and every row selected = the full backward
+    full = orc.hybrid_attention_backward(Q, K, V, dO, modes, cu, n_sink=1, window_blocks=2)
+    allt = np.arange(T)
+    rows = orc.hybrid_attention_backward_rows(Q, K, V, dO, modes, cu, allt, allt, n_sink=1,
+                                              window_blocks=2)
+    for a, r in zip(rows, full):
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-11)
+
+
 def test_backward_finite_differences():
     L, Hq, Hkv, d = 70, 2, 1, 4
     cu = np.array([0, L])
