@@ -16,7 +16,10 @@ against the MI355X dense bf16 MFMA peak.  `traffic` is that kernel's HBM bytes
 per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by what the
 same counters read for an elementwise kernel of known size), read from
 profiles/attention_traffic.json when it was taken on the current kernel
-source, else null.  `mfma_loop_tflops` is the practical ceiling beside the
+source, else null.  `mfma_busy` is the share of SIMD-cycles in which that
+kernel's matrix pipe is busy (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over
+GRBM_GUI_ACTIVE x 1024 SIMDs / 8 XCDs), from
+profiles/attention_sq_counters.json under the same source-hash rule.  `mfma_loop_tflops` is the practical ceiling beside the
 data-sheet peak: the library's MFMA-loop probe (8 waves per CU issuing
 back-to-back bf16 MFMAs with no memory traffic) at whatever clock the board
 holds under that load, measured in the same run.
@@ -49,6 +52,8 @@ ATTN_SRCS = [os.path.join(ROOT, "full_attention_long_amd", "csrc", f)
              for f in ("ea_attention.hip", "ea_worklist.hip")]
 ATTN_HEADER = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_internal.h")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attention_traffic.json")
+SQ_JSON = os.path.join(ROOT, "profiles", "attention_sq_counters.json")
+N_XCD, N_SIMD = 8, 1024   # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 ATTN_KERNEL = "attention_kernel"
 CALIB_KERNEL = "bitwise_not"
 
@@ -159,6 +164,42 @@ def stored_traffic():
     return t
 
 
+def stored_sq():
+    """Matrix-pipe utilisation of the attention kernel from the stored SQ
+    counter summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(SQ_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t
+
+
+def cpu_info():
+    """Host CPU model and the cores this process may run on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def pin_blas(cores):
+    """Limit the BLAS thread pools to `cores` threads (returns the limiter)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        return None
+
+
 def cpu_baseline(cases, budget_s=12.0):
     """The oracle on a bounded sample of the same layers: 64-row query blocks
     of one query head at seeded positions, alternating between the layers,
@@ -167,13 +208,13 @@ def cpu_baseline(cases, budget_s=12.0):
     from full_attention_long_amd import metrics
     from oracle import ea_oracle as orc
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    model, cores = cpu_info()
+    limiter = pin_blas(cores)
     rng = np.random.default_rng(0)
     f32 = [(c.q_f32(), c.k_f32(), c.v_f32()) for c in cases]
+    total_flops = sum(metrics.effective_flops(c.target_modes, c.lengths, c.Hq, c.Hkv, c.d,
+                                              n_sink=c.n_sink, keep_fraction=c.keep_fraction)
+                      for c in cases)
     done_flops, units, t_used = 0, 0, 0.0
     while t_used < budget_s and units < 512:
         ci = units % len(cases)
@@ -193,12 +234,18 @@ def cpu_baseline(cases, budget_s=12.0):
         nvis = qb + 1 if c.target_modes[0, g] == 0 else min(qb + 1, c.n_sink + w)
         done_flops += 4 * c.d * len(toks) * 64 * nvis
         units += 1
+    if limiter is not None:
+        limiter.restore_original_limits()
+    frac = done_flops / total_flops
     return {
         "value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-        "kind": "oracle",
+        "kind": "oracle", "precision": "float64", "cpu_model": model,
+        "sample_fraction": round(frac, 6), "extrapolated": bool(frac < 0.05),
         "sample": f"{units} query blocks of 64 rows x one query head at seeded positions, "
-                  f"alternating {'+'.join(c.name for c in cases)}; float64 two-pass softmax over "
-                  f"the visible keys; {t_used:.1f} s of CPU; {platform.machine()} host",
+                  f"alternating {'+'.join(c.name for c in cases)} ({100 * frac:.3f}% of the "
+                  f"step's effective FLOPs; the rate is extrapolated from it); float64 two-pass "
+                  f"softmax over the visible keys on {cores} cores (BLAS threads pinned to "
+                  f"them); {t_used:.1f} s of CPU",
     }
 
 
@@ -209,11 +256,8 @@ def cpu_baseline_dual(c, budget_s=12.0):
     (the dual forward's effective work) over its wall time."""
     from oracle import ea_oracle as orc
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    model, cores = cpu_info()
+    limiter = pin_blas(cores)
     rng = np.random.default_rng(0)
     qf, kf, vf = c.q_f32(), c.k_f32(), c.v_f32()
     L = int(c.lengths[0])
@@ -230,12 +274,14 @@ def cpu_baseline_dual(c, budget_s=12.0):
         t_used += time.perf_counter() - t0
         done_flops += 4 * c.d * len(toks) * 64 * (qb + 1)
         units += 1
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {
         "value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-        "kind": "oracle",
+        "kind": "oracle", "precision": "float64", "cpu_model": model, "extrapolated": True,
         "sample": f"{units} query blocks of 64 rows x one query head at seeded positions of "
-                  f"{c.name}, each in both modes; float64 two-pass softmax; {t_used:.1f} s of "
-                  f"CPU; {platform.machine()} host",
+                  f"{c.name}, each in both modes; float64 two-pass softmax on {cores} cores; "
+                  f"{t_used:.1f} s of CPU",
     }
 
 
@@ -487,11 +533,8 @@ def cpu_baseline_xa(c, cmodes, budget_s=12.0):
     wall time."""
     from oracle import xa_oracle as xo
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    model, cores = cpu_info()
+    limiter = pin_blas(cores)
     from workloads import gen
     rng = np.random.default_rng(0)
     G = c.Hq // c.Hkv
@@ -518,13 +561,15 @@ def cpu_baseline_xa(c, cmodes, budget_s=12.0):
         t_used += time.perf_counter() - t0
         done_flops += 4 * c.d * len(rows) * len(cols)
         units += 1
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {
         "value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-        "kind": "oracle",
+        "kind": "oracle", "precision": "float64", "cpu_model": model, "extrapolated": True,
         "sample": f"{units} XA query blocks of 128 rows x one query head at seeded positions of "
                   f"{c.name}: block masses of the row, threshold selection, float64 attention "
-                  f"over the kept blocks; FLOPs of the kept blocks; {t_used:.1f} s of CPU; "
-                  f"{platform.machine()} host",
+                  f"over the kept blocks; FLOPs of the kept blocks; {cores} cores; {t_used:.1f} s "
+                  f"of CPU",
     }
 
 
@@ -707,6 +752,40 @@ def summarize_counters(pmc_dirs, calib_mib, layers_flops, out_path):
     print(json.dumps(out, indent=1))
 
 
+def summarize_sq(pmc_dirs, layers, out_path):
+    """Turn rocprofv3 --pmc CSV output holding SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE (any further counters are kept too) into the stored
+    matrix-pipe summary: means per attention dispatch and the busy share of
+    SIMD-cycles."""
+    import csv
+    means = {}
+    for d in pmc_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = []
+        for fn in files:
+            with open(fn) as f:
+                rows += list(csv.DictReader(f))
+        for counter in {r["Counter_Name"] for r in rows}:
+            att = [float(r["Counter_Value"]) for r in rows
+                   if r["Counter_Name"] == counter and ATTN_KERNEL in r["Kernel_Name"]]
+            if att:
+                means[counter] = {"per_dispatch": sum(att) / len(att), "dispatches": len(att)}
+    need = ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+    if any(n not in means for n in need):
+        raise SystemExit(f"need counters {need}; found {sorted(means)}")
+    simd_cycles = means["GRBM_GUI_ACTIVE"]["per_dispatch"] / N_XCD * N_SIMD
+    busy = means["SQ_VALU_MFMA_BUSY_CYCLES"]["per_dispatch"] / simd_cycles
+    out = {"kernel": ATTN_KERNEL, "kernel_source_sha256_16": kernel_source_hash(),
+           "counters": means, "simd_cycles_per_dispatch": simd_cycles,
+           "mfma_busy": busy, "layers": layers}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -739,7 +818,14 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="PMC_DIR",
                     help="no GPU work: turn rocprofv3 --pmc output directories of a run made with "
                          "--calibrate-mib into profiles/attention_traffic.json")
+    ap.add_argument("--summarize-sq", nargs="+", default=None, metavar="PMC_DIR",
+                    help="no GPU work: turn rocprofv3 --pmc output directories holding "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE into "
+                         "profiles/attention_sq_counters.json")
     args = ap.parse_args()
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.runs, SQ_JSON)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.calibrate_mib or 1024, args.runs,
                            TRAFFIC_JSON)
@@ -839,6 +925,8 @@ def main():
     traffic = None
     if tr is not None:
         traffic = round(float(tr["hbm_bytes_per_launch"]), 0)
+    sq = stored_sq()
+    mfma_busy = round(float(sq["mfma_busy"]), 4) if sq is not None else None
     log(f"step {step_ms:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
         f"attention {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of peak")
     out = {
@@ -855,7 +943,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "mfma_busy": mfma_busy,
             "kernel": "ea::attention_kernel_bf16<128, false>",
             "avg_launch_ms": round(attn_sum / len(runs), 4),
             "flops_per_launch": round(tot_ef / len(runs), 0),
