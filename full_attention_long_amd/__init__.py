@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     ea_hybrid_backward,
     ea_hybrid_backward_workspace_size,
     ea_hybrid_prefill,
+    ea_hybrid_prefill_noalloc,
+    ea_hybrid_prefill_noalloc_max_workspace,
     ea_hybrid_prefill_plan,
     ea_hybrid_prefill_plan_layout,
     ea_hybrid_prefill_run,

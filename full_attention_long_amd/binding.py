@@ -89,6 +89,11 @@ def lib() -> ctypes.CDLL:
     L.ea_hybrid_prefill.restype = i32
     L.ea_hybrid_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
                                     ctypes.POINTER(SparsityParams), vp, vp, vp, sz, vp]
+    L.ea_hybrid_prefill_noalloc_max_workspace.restype = sz
+    L.ea_hybrid_prefill_noalloc_max_workspace.argtypes = []
+    L.ea_hybrid_prefill_noalloc.restype = i32
+    L.ea_hybrid_prefill_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                            ctypes.POINTER(SparsityParams), vp, vp, vp]
     L.ea_hybrid_prefill_plan_layout.restype = i32
     L.ea_hybrid_prefill_plan_layout.argtypes = [i32, i64, i32, i32, i32, i32, i32,
                                                 ctypes.POINTER(i64), ctypes.POINTER(i64),
@@ -319,6 +324,33 @@ def ea_hybrid_prefill(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: in
                                    B, T, max_seqlen, Hq, Hkv, d, ctypes.byref(sp), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def ea_hybrid_prefill_noalloc(Q, K, V, modes, cu_seqlens, max_seqlen: int, *, n_sink: int = 1,
+                              window_blocks: int = 0, keep_fraction: float = 0.2,
+                              softmax_scale: float = 0.0, block: int = 64, out, lse=None,
+                              stream=None):
+    """ea_hybrid_prefill into caller-provided ``out`` (and ``lse``) with the
+    library's static workspace: the call allocates nothing (not even here)."""
+    import torch
+    T, Hq, Hkv, d = _check_qkv(Q, K, V)
+    B = _check_cu(cu_seqlens)
+    _meta(modes, "modes", (torch.int8,), shape=(B, Hkv))
+    _meta(out, "out", (Q.dtype,), shape=Q.shape)
+    if lse is not None:
+        _meta(lse, "lse", (torch.float32,), shape=(Hq, T))
+    for t, n in [(Q, "Q"), (K, "K"), (V, "V"), (modes, "modes"), (cu_seqlens, "cu_seqlens"),
+                 (out, "out")]:
+        _dev(t, n)
+    sp = SparsityParams(block, n_sink, window_blocks, keep_fraction, softmax_scale)
+    _check(lib().ea_hybrid_prefill_noalloc(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(modes),
+                                           _ptr(cu_seqlens), B, T, max_seqlen, Hq, Hkv, d,
+                                           ctypes.byref(sp), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def ea_hybrid_prefill_noalloc_max_workspace() -> int:
+    return int(lib().ea_hybrid_prefill_noalloc_max_workspace())
 
 
 def ea_hybrid_prefill_plan_layout(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype_code):

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -279,11 +280,17 @@ ea_status ea_hybrid_prefill_run(const void* Q, const void* K, const void* V, ea_
   return ok();
 }
 
-ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
-                            const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
-                            int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
-                            int32_t head_dim, const ea_sparsity_params* p, void* O, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The one-shot prefill; `validate` lets EA_VALIDATE make the call wait for
+// the device-content checks (the allocation-free entry point never waits).
+ea_status prefill_impl(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                       const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                       int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                       int32_t head_dim, const ea_sparsity_params* p, void* O, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream, bool validate) {
   ea::Shape s;
   ea::Workspace ws;
   ea::Geometry g;
@@ -296,11 +303,75 @@ ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtyp
   char* base = static_cast<char*>(workspace);
   hipError_t e = ea::launch_worklist(s, g, modes, cu_seqlens, ws, base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-  if (validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
+  if (validate && validate_on() && (st = workspace_verdict(workspace, stream)) != EA_OK) return st;
   e = ea::launch_attention(s, g, Q, K, V, cu_seqlens, ea::AttnOut{O, lse, nullptr, nullptr}, ws,
                            base, hs);
   if (e != hipSuccess) return fail(EA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Workspace of the allocation-free prefill: one static array per GPU, held
+// until the process ends.  In host code the array's name only stands for the
+// device symbol; its device address comes from hipGetSymbolAddress, once per
+// device (each GPU holds its own copy at its own address).
+constexpr size_t kNoAllocBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ea_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(EA_ERR_UNSUPPORTED, "device index %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(EA_ERR_HIP, "hipGetSymbolAddress of the static workspace failed: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status ea_hybrid_prefill(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                            const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                            int64_t total_tokens, int32_t max_seqlen, int32_t Hq, int32_t Hkv,
+                            int32_t head_dim, const ea_sparsity_params* p, void* O, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(Q, K, V, dtype, modes, cu_seqlens, B, total_tokens, max_seqlen, Hq, Hkv,
+                      head_dim, p, O, lse, workspace, workspace_bytes, stream, true);
+}
+
+size_t ea_hybrid_prefill_noalloc_max_workspace(void) { return kNoAllocBytes; }
+
+ea_status ea_hybrid_prefill_noalloc(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                                    const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                                    int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, const ea_sparsity_params* p,
+                                    void* O, float* lse, void* stream) {
+  ea::Shape s;
+  ea_status st = check_shape(B, total_tokens, max_seqlen, Hq, Hkv, head_dim, dtype, &s);
+  if (st != EA_OK) return st;
+  const size_t need = ea::plan_workspace(s).total;
+  if (need > kNoAllocBytes)
+    return fail(EA_ERR_WORKSPACE,
+                "these sizes need %zu bytes of workspace; the static workspace of the "
+                "allocation-free prefill holds %zu (use ea_hybrid_prefill with a workspace)",
+                need, kNoAllocBytes);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != EA_OK) return st;
+  return prefill_impl(Q, K, V, dtype, modes, cu_seqlens, B, total_tokens, max_seqlen, Hq, Hkv,
+                      head_dim, p, O, lse, ws, kNoAllocBytes, stream, false);
 }
 
 ea_status ea_gumbel_route(const float* logits, const float* gumbel, float tau, int32_t n,

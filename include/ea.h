@@ -157,6 +157,28 @@ size_t ea_hybrid_prefill_workspace_size(int32_t B, int64_t total_tokens, int32_t
                                         int32_t Hq, int32_t Hkv, int32_t head_dim,
                                         ea_dtype dtype);
 
+/* ea_hybrid_prefill_noalloc - ea_hybrid_prefill for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and results without
+ * the workspace, which is instead a static array of
+ * ea_hybrid_prefill_noalloc_max_workspace() bytes (4 MiB) inside the library,
+ * one per GPU, held until the process ends.  The call allocates nothing.
+ *
+ * Sizes whose workspace (ea_hybrid_prefill_workspace_size) exceeds that
+ * array return EA_ERR_WORKSPACE before anything is launched; 4 MiB covers,
+ * with 8 KV heads and 4 query heads per KV head, about 1.2 million tokens.
+ * Every call on a GPU uses that GPU's one array, so calls that overlap on
+ * one GPU (concurrent streams, threads) race and must be ordered by the
+ * caller.  Nothing in the array needs to start at any value: each call
+ * writes what it reads.  EA_VALIDATE does not make this call wait (it never
+ * synchronises); ea_workspace_status cannot see its workspace. */
+size_t ea_hybrid_prefill_noalloc_max_workspace(void);
+ea_status ea_hybrid_prefill_noalloc(const void* Q, const void* K, const void* V, ea_dtype dtype,
+                                    const int8_t* modes, const int32_t* cu_seqlens, int32_t B,
+                                    int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, const ea_sparsity_params* p,
+                                    void* O, float* lse, void* stream);
+
 /* ea_hybrid_prefill_plan_layout - where ea_hybrid_prefill_plan (and the
  * one-shot call) put the work list inside a workspace of these sizes, for
  * inspection.  Byte offsets of: the item records (n_slots records of five

@@ -24,7 +24,8 @@ def test_every_header_function_is_exported():
                           "ea_router_logit_grad_workspace_size", "ea_router_logit_grad",
                           "ea_xa_prefill_workspace_size", "ea_xa_prefill",
                           "ea_xa_prefill_plan", "ea_xa_prefill_run", "ea_workspace_status",
-                          "ea_hybrid_prefill_plan_layout"}
+                          "ea_hybrid_prefill_plan_layout", "ea_hybrid_prefill_noalloc",
+                          "ea_hybrid_prefill_noalloc_max_workspace"}
     L = ea.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -374,3 +375,20 @@ def test_plan_layout_is_inside_the_workspace():
         assert spans[0][0] >= 256          # after the header
     with pytest.raises(ea.EAError):
         ea.ea_hybrid_prefill_plan_layout(0, 10, 10, 8, 2, 64, 1)
+
+
+def test_noalloc_rejects_sizes_beyond_its_static_workspace():
+    L = ea.lib()
+    cap = ea.ea_hybrid_prefill_noalloc_max_workspace()
+    assert cap == 4 << 20
+    sp = bnd.SparsityParams(64, 1, 0, 0.2, 0.0)
+    # 4M tokens x 8 KV heads need far more than 4 MiB of work list
+    st = L.ea_hybrid_prefill_noalloc(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, 2**22, 2**17, 32, 8, 128,
+                                     ctypes.byref(sp), FAKE, None, None)
+    assert st == bnd.EA_ERR_WORKSPACE and "static workspace" in ea.ea_last_error()
+    # the 128K headline layer fits
+    assert ea.ea_hybrid_prefill_workspace_size(1, 131072, 131072, 32, 8, 128, 1) <= cap
+    # invalid sizes are rejected before any device call
+    st = L.ea_hybrid_prefill_noalloc(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 0, 10, 10, 8, 2, 128,
+                                     ctypes.byref(sp), FAKE, None, None)
+    assert st == bnd.EA_ERR_INVALID_ARG
