@@ -15,13 +15,15 @@
 // Three kernels: bwd_pre_kernel (D and LSE in log2 units per row),
 // bwd_dq_kernel (query-tile stationary, the forward's work list and K/V
 // tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with 32x32x16 MFMAs)
-// and bwd_dkv_kernel (key stationary, launched once per output: each wave
-// owns 32 keys of its KV head and walks the query blocks that can see them,
-// head by head: S = Q K^T and dV += P^T dO, or S, dP = dO V^T and
-// dK += dS^T Q, with 16x16x32 MFMAs).
+// and bwd_dkv_kernel (key stationary: each pair of waves owns 32 keys of its
+// KV head and walks the query blocks that can see them, head by head, one
+// wave computing S, P and dV += P^T dO, the other dP and dK += dS^T Q, with
+// 16x16x32 MFMAs).
 #include "ea_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 
 namespace ea {
@@ -273,221 +275,329 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: a workgroup owns kDkvKeys keys of one KV head of one sequence, 32
-// per wave as two 16-key tiles, and walks the query blocks that can see them;
-// for each query block and each of the G query heads it stages that head's Q
-// and dO rows, LSE and D in LDS (the next stage prefetched into registers).
-// Two launches split the work by role: ROLE 0 rebuilds P and accumulates
-// dV += P^T dO, ROLE 1 rebuilds P and dP and accumulates dK += dS^T Q.  Each
-// Q / dO operand read from LDS feeds the MFMAs of both key tiles, so a role
-// reads half the LDS bytes per product that one wave owning 16 keys of both
-// outputs did; the price is S computed by both roles (five products per key
-// and query instead of four), and each role fits two waves per SIMD.
+// dK, dV: a workgroup owns kDkvKeys keys of one KV head of one sequence and
+// walks the query blocks that can see them, each block once per query head of
+// the group: tile t = (block qb_hi - t / G, head t % G) is that head's 64 Q
+// and dO rows with their LSE and D.  The walk runs downwards from the last
+// block, where every key chunk of a head starts, so the workgroups of one head
+// that run together read the same Q and dO tiles at about the same time and
+// share them in the cache.  The 8 waves form 4 pairs, waves p and
+// p + 4 (one SIMD), each pair owning 32 keys as two 16-key tiles, and split
+// the work of a tile in two balanced halves:
+//   wave p     (A): S = Q K^T, P = exp(S - LSE) (bf16) into LDS, dV += P^T dO;
+//   wave p + 4 (B): dP = dO V^T, dS = P (dP - D) with P from LDS, dK += dS^T Q.
+// S and dP are formed once per key and query (four products instead of the
+// five of separate dK and dV kernels), and each Q / dO operand read from LDS
+// feeds the MFMAs of both key tiles.  B works one tile behind A, so a single
+// barrier per step orders everything: in step k, A takes tile k, B tile k - 1
+// (whose P A wrote in step k - 1), and all threads write tile k + 1 from
+// registers into the third buffer of a three-tile LDS ring, then load tile
+// k + 2 into those registers.
 // ---------------------------------------------------------------------------
 constexpr int kDkvThreads = 64 * kDkvWaves;
-constexpr int kDkvKeysPerWave = kDkvKeys / kDkvWaves;
-static_assert(kDkvKeysPerWave == 32, "two 16-key tiles per wave");
+constexpr int kDkvPairs = kDkvWaves / 2;
+static_assert(kDkvKeys == 32 * kDkvPairs, "two 16-key tiles per wave pair");
 
-template <int D, int ROLE>
+template <int D>
 __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int NU = D / 32;    // 32-wide d steps
   constexpr int NM = D / 16;    // 16-wide d tiles of dK, dV
   constexpr int QROW = D + 16;  // padded LDS rows of the Q and dO tiles
+  constexpr int TILE = kBlock * QROW;
   constexpr int NCH = kBlock * D / 8 / kDkvThreads;  // 16-byte chunks per thread per tile
   static_assert(NCH * kDkvThreads * 8 == kBlock * D, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBlock * QROW], Os[kBlock * QROW];
-  __shared__ __attribute__((aligned(16))) float Ls[kBlock], Ds[kBlock];
+  // ring of 3 tiles: [buffer][Q, dO] rows, [buffer][LSE, D]
+  __shared__ __attribute__((aligned(16))) uint16_t Ts[3][2][TILE];
+  __shared__ __attribute__((aligned(16))) float Ls[3][2][kBlock];
+  // P of each pair as bf16 A operands: [tile parity][pair][2 half + key tile][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 Px[2][kDkvPairs][4][64];
 
-  // raw item ((b Hkv + g) npair + pair), taken in the list's cost order
-  const int64_t item = a.dkv_order[blockIdx.x];
-  const int pair = static_cast<int>(item % a.npair);
+  // raw item ((b Hkv + g) npair + grp), taken in the list's cost order, in
+  // chunks of consecutive entries per XCD: within a cost band the list holds
+  // the key chunks of one head in a row, so those share the XCD's cache
+  const int64_t pos = list_position(blockIdx.x);
+  if (pos >= a.dkv_n) return;
+  const int64_t item = a.dkv_order[pos];
+  const int grp = static_cast<int>(item % a.npair);
   const int64_t rest = item / a.npair;
   const int g = static_cast<int>(rest % a.Hkv);
   const int b = static_cast<int>(rest / a.Hkv);
   if (a.meta[kMetaStamp] != a.stamp) return;  // the planner rejected the device contents
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  if (pair * kDkvKeys >= L) return;
+  if (grp * kDkvKeys >= L) return;
   const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + g] != 0 ? kModeSA : kModeFA;
   const int ns = a.n_sink, w = a.seq_w[b];
   const int N = (L + kBlock - 1) / kBlock;
-  const int kb0 = pair * (kDkvKeys / kBlock);
+  const int kb0 = grp * (kDkvKeys / kBlock);
   const int kb1 = min(N - 1, kb0 + kDkvKeys / kBlock - 1);
   const int qb_lo = kb0;
   const int qb_hi = (mode == kModeSA && kb0 >= ns) ? min(N - 1, kb1 + w - 1) : N - 1;
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64, lg = lane / 16, li = lane % 16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, lg = lane / 16, li = lane % 16;
+  const bool role_a = wave < kDkvPairs;  // wave-uniform
+  const int pw = wave % kDkvPairs;       // the pair, and its 32 keys
   // this lane's key of key tile c as a B column, and its block
   int key_b[2], kbj[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    key_b[c] = pair * kDkvKeys + wave * kDkvKeysPerWave + 16 * c + li;
+    key_b[c] = grp * kDkvKeys + pw * 32 + 16 * c + li;
     kbj[c] = key_b[c] / kBlock;
   }
-  // K (both roles) and V (ROLE 1) rows as the B operands of S = Q K^T and
-  // dP = dO V^T
-  bf16x8 kf[2][NU], vf[2][NU];
+  // K (wave A) or V (wave B) rows as the B operands of S = Q K^T or dP = dO V^T
+  bf16x8 bfr[2][NU];
+  {
+    const uint16_t* src = role_a ? a.K : a.V;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const bool kv = key_b[c] < L;
-    const int64_t r = (static_cast<int64_t>(tok0 + (kv ? key_b[c] : 0)) * a.Hkv + g) * D;
+    for (int c = 0; c < 2; ++c) {
+      const bool kv = key_b[c] < L;
+      const int64_t r = (static_cast<int64_t>(tok0 + (kv ? key_b[c] : 0)) * a.Hkv + g) * D;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      kf[c][u] = kv ? *reinterpret_cast<const bf16x8*>(a.K + r + 32 * u + 8 * lg) : bf16x8{};
-      if constexpr (ROLE == 1)
-        vf[c][u] = kv ? *reinterpret_cast<const bf16x8*>(a.V + r + 32 * u + 8 * lg) : bf16x8{};
+      for (int u = 0; u < NU; ++u)
+        bfr[c][u] = kv ? *reinterpret_cast<const bf16x8*>(src + r + 32 * u + 8 * lg) : bf16x8{};
     }
   }
-  f32x4 acc[2][NM];  // dV (ROLE 0) or dK (ROLE 1)
+  f32x4 acc[2][NM];  // dV (wave A) or dK (wave B)
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[c][m] = f32x4{};
   const float cl = a.scale * kLog2e;
 
-  // stage (qb, hh) -> registers, two stages ahead (set x holds the stages
-  // of parity x), so a stage's loads have two steps of work to land in
-  u32x4 qreg[2][NCH], oreg[2][NCH];
-  float lreg[2] = {0.f, 0.f}, dreg[2] = {0.f, 0.f};
-  auto fetch = [&](int x, int st) {
-    const int qb = qb_lo + st / a.G;
-    const int hq = g * a.G + st % a.G;
+  // tile t -> registers -> ring buffer
+  u32x4 qreg[NCH], oreg[NCH];
+  float lreg = 0.f, dreg = 0.f;
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int qb = qb_hi - t / a.G;
+    const int hq = g * a.G + t % a.G;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
       const int p = qb * kBlock + r;
       const int64_t src = (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + col;
-      qreg[x][k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
-      oreg[x][k] = p < L ? *reinterpret_cast<const u32x4*>(a.dO + src) : u32x4{0, 0, 0, 0};
+      qreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
+      oreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.dO + src) : u32x4{0, 0, 0, 0};
     }
     if (tid < kBlock) {
       const int p = qb * kBlock + tid;
       const int64_t ix = static_cast<int64_t>(hq) * a.T + tok0 + p;
-      lreg[x] = p < L ? a.lse2[ix] : INFINITY;
-      if constexpr (ROLE == 1) dreg[x] = p < L ? a.Dv[ix] : 0.f;
+      lreg = p < L ? a.lse2[ix] : INFINITY;
+      dreg = p < L ? a.Dv[ix] : 0.f;
     }
   };
-  auto stage = [&](int x) {
+  auto stage = [&](int t) __attribute__((always_inline)) {
+    const int buf = t % 3;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Qs + r * QROW + col) = qreg[x][k];
-      *reinterpret_cast<u32x4*>(Os + r * QROW + col) = oreg[x][k];
+      *reinterpret_cast<u32x4*>(&Ts[buf][0][r * QROW + col]) = qreg[k];
+      *reinterpret_cast<u32x4*>(&Ts[buf][1][r * QROW + col]) = oreg[k];
     }
     if (tid < kBlock) {
-      Ls[tid] = lreg[x];
-      Ds[tid] = dreg[x];
+      Ls[buf][0][tid] = lreg;
+      Ls[buf][1][tid] = dreg;
     }
   };
 
-  const int nsteps = (qb_hi - qb_lo + 1) * a.G;
-  fetch(0, 0);
-  if (nsteps > 1) fetch(1, 1);
-  // one step of the walk; x = st & 1, written out per parity so that the
-  // register sets are named statically
-  auto step = [&](int st, int x) {
-    const int qb = qb_lo + st / a.G;
-    __syncthreads();  // the previous step's reads of the tiles are done
-    stage(x);
-    __syncthreads();
-    if (st + 2 < nsteps) fetch(x, st + 2);
-
-    // whether every row of query block qb sees every key of key tile c (the
-    // tile's 16 keys share one 64-key block; wave-uniform)
-    bool full[2];
+  // The products of a half hf (the tile's query rows 32 hf .. 32 hf + 31):
+  //  rows: S = Q K^T (wave A) or dP = dO V^T (wave B), 2 query tiles of 16
+  //        rows x 2 key tiles; lane holds key li of tile c, rows 16 qt + 4 lg + i;
+  //  cols: acc += X^T T with X (P for wave A, dS for wave B) as bf16 A
+  //        operands (keys x the half's 32 queries) and T (dO, Q) by
+  //        transposing reads, query rows 32 hf + 4 lg + 0..3 and + 16, the
+  //        order the operands hold them in.
+  // Each operand read from LDS feeds both key tiles.  Reads are issued as a
+  // group ahead of their MFMAs (load_* / mma_*), so the waves' LDS latency
+  // hides behind other work.
+  typedef bf16x8 RowOps[2][NU];
+  typedef bf16x8 ColOps[NM];
+  auto load_rows = [&](const uint16_t* src, int hf, RowOps& qa) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int klast = pair * kDkvKeys + wave * kDkvKeysPerWave + 16 * c + 15;
-      full[c] = klast <= qb * kBlock && qb * kBlock + kBlock <= L &&
-                (mode == kModeFA || kbj[c] < ns || qb - kbj[c] < w);
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        qa[t2][u] = *reinterpret_cast<const bf16x8*>(src + (16 * (2 * hf + t2) + li) * QROW + 32 * u + 8 * lg);
+  };
+  auto mma_rows = [&](const RowOps& qa, f32x4 (*x)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) x[t2][c] = f32x4{};
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) x[t2][c] = mfma16(qa[t2][u], bfr[c][u], x[t2][c]);
     }
-    // Two halves of 32 query rows; per half, S (and dP) as 2 query tiles of
-    // 16 rows x 2 key tiles: lane holds key li of tile c, rows 16 qt + 4 lg + i
+  };
+  auto load_cols = [&](const uint16_t* src, int hf, ColOps& bt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int off = (32 * hf + 4 * lg + li / 4) * QROW + 16 * m + 4 * (li & 3);
+      bt[m] = tr_pair(src + off, src + off + 16 * QROW);
+    }
+  };
+  // m in [m0, m1)
+  auto mma_cols = [&](const bf16x8* xa, const ColOps& bt, int m0, int m1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = m0; m < m1; ++m)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[c][m] = mfma16(xa[c], bt[m], acc[c][m]);
+  };
+  auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+
+  // wave A, tile t: P = exp(S - LSE) as bf16, to LDS for wave B, and
+  // dV += P^T dO.  MASKED: some key of the pair is invisible to some row of
+  // the block (the diagonal block, the window's edge, the sequence's end); the
+  // mask then sends the exponent to -inf.  `between` runs after the first
+  // half's MFMAs are issued.
+  auto tile_a = [&](int t, auto masked, auto between) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int qb = qb_hi - t / a.G;
+    const uint16_t* Qt = Ts[t % 3][0];
+    const uint16_t* Ot = Ts[t % 3][1];
+    const float* Lt = Ls[t % 3][0];
+    RowOps qa;
+    ColOps bt;
+    load_rows(Qt, 0, qa);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      f32x4 s[2][2], dp[2][2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int qt = 2 * hf + t2;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          s[t2][c] = f32x4{};
-          dp[t2][c] = f32x4{};
-        }
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int off = (16 * qt + li) * QROW + 32 * u + 8 * lg;
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + off);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) s[t2][c] = mfma16(qa, kf[c][u], s[t2][c]);
-          if constexpr (ROLE == 1) {
-            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Os + off);
-#pragma unroll
-            for (int c = 0; c < 2; ++c) dp[t2][c] = mfma16(oa, vf[c][u], dp[t2][c]);
-          }
-        }
-      }
-      // P (ROLE 0) or dS (ROLE 1) as bf16 A operands: keys x the half's 32
-      // queries, in the order the transposed B reads deliver them.  A key
-      // tile that every row of the query block sees (below the diagonal,
-      // inside the window, rows before the sequence end: the common case)
-      // skips the per-element visibility test.
+      f32x4 s[2][2];
+      fence();
+      mma_rows(qa, s);
+      fence();
+      load_cols(Ot, hf, bt);
+      fence();
       bf16x8 pa[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int qt = 2 * hf + t2;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * qt + 4 * lg);
-        f32x4 dv4 = f32x4{};
-        if constexpr (ROLE == 1) dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * qt + 4 * lg);
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(Lt + 16 * qt + 4 * lg);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          f32x4 pv;
-          if (full[c]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][c][i], cl, -lv[i]));
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 4; ++i) {
+            float e = __builtin_fmaf(s[t2][c][i], cl, -lv[i]);
+            if constexpr (MASKED) {
               const int p = qb * kBlock + 16 * qt + 4 * lg + i;
               const bool vis = key_b[c] <= p && p < L &&
                                (mode == kModeFA || kbj[c] < ns || p / kBlock - kbj[c] < w);
-              pv[i] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][c][i], cl, -lv[i])) : 0.f;
+              e = vis ? e : -INFINITY;
             }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (ROLE == 0) pa[c][4 * t2 + i] = static_cast<__bf16>(pv[i]);
-            else pa[c][4 * t2 + i] = static_cast<__bf16>(pv[i] * (dp[t2][c][i] - dv4[i]));
+            pa[c][4 * t2 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(e));
           }
         }
       }
-      // dV += P^T dO (ROLE 0) or dK += dS^T Q (ROLE 1): B from the tiles by
-      // transposing reads, query rows 32 hf + 4 lg + 0..3 and + 16, the order
-      // pa holds them in; each read feeds both key tiles
-      const uint16_t* src = ROLE == 0 ? Os : Qs;
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const int off = (32 * hf + 4 * lg + li / 4) * QROW + 16 * m + 4 * (li & 3);
-        const bf16x8 bt = tr_pair(src + off, src + off + 16 * QROW);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) acc[c][m] = mfma16(pa[c], bt, acc[c][m]);
-      }
+      for (int c = 0; c < 2; ++c) Px[t & 1][pw][2 * hf + c][lane] = pa[c];
+      fence();
+      mma_cols(pa, bt, 0, NM / 2);
+      fence();
+      if (hf == 0) load_rows(Qt, 1, qa);  // into the registers the first MFMAs freed
+      fence();
+      mma_cols(pa, bt, NM / 2, NM);
+      fence();
+      if (hf == 0) between();
     }
   };
-  for (int st = 0; st < nsteps; st += 2) {
-    step(st, 0);
-    if (st + 1 < nsteps) step(st + 1, 1);
+  // wave B, tile t: dS = P (dP - D), then dK += dS^T Q
+  auto tile_b = [&](int t, auto between) __attribute__((always_inline)) {
+    const uint16_t* Qt = Ts[t % 3][0];
+    const uint16_t* Ot = Ts[t % 3][1];
+    const float* Dt = Ls[t % 3][1];
+    RowOps qa;
+    ColOps bt;
+    load_rows(Ot, 0, qa);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 dp[2][2];
+      fence();
+      mma_rows(qa, dp);
+      fence();
+      load_cols(Qt, hf, bt);
+      bf16x8 pa[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) pa[c] = Px[t & 1][pw][2 * hf + c][lane];
+      f32x4 dv4[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) dv4[t2] = *reinterpret_cast<const f32x4*>(Dt + 16 * (2 * hf + t2) + 4 * lg);
+      fence();
+      bf16x8 ds[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ds[c][4 * t2 + i] =
+                static_cast<__bf16>(static_cast<float>(pa[c][4 * t2 + i]) * (dp[t2][c][i] - dv4[t2][i]));
+      fence();
+      mma_cols(ds, bt, 0, NM / 2);
+      fence();
+      if (hf == 0) load_rows(Ot, 1, qa);
+      fence();
+      mma_cols(ds, bt, NM / 2, NM);
+      fence();
+      if (hf == 0) between();
+    }
+  };
+
+  const int nsteps = (qb_hi - qb_lo + 1) * a.G;
+  fetch(0);
+  stage(0);
+  if (nsteps > 1) fetch(1);
+  __syncthreads();
+  // Step k: wave A takes tile k and wave B tile k - 1; between their halves
+  // all threads write tile k + 1 (loaded a step earlier) into the ring and
+  // start the loads of tile k + 2.  Both roles pass nsteps + 1 barriers.
+  auto ring = [&](int k) __attribute__((always_inline)) {
+    if (k + 1 < nsteps) {
+      stage(k + 1);
+      if (k + 2 < nsteps) fetch(k + 2);
+    }
+  };
+  if (role_a) {
+    // Every row of block qb sees every key of the pair exactly when
+    // kbj < qb <= qf: past the diagonal block, inside the sequence's whole
+    // blocks and, for a window, inside the window.  Those tiles (qb walks
+    // down, so a middle range of k) take the unmasked variant; each variant
+    // runs in a loop of its own, so each is register-allocated alone.
+    int qf = L / kBlock - 1;
+    if (mode == kModeSA && kbj[0] >= ns) qf = min(qf, kbj[0] + w - 1);
+    const int m1 = min(nsteps, max(0, (qb_hi - kbj[0]) * a.G));
+    const int m0 = min(m1, max(0, (qb_hi - qf) * a.G));
+    int k = 0;
+    for (; k < m0; ++k) {
+      tile_a(k, std::true_type{}, [&]() __attribute__((always_inline)) { ring(k); });
+      __syncthreads();
+    }
+    for (; k < m1; ++k) {
+      tile_a(k, std::false_type{}, [&]() __attribute__((always_inline)) { ring(k); });
+      __syncthreads();
+    }
+    for (; k < nsteps; ++k) {
+      tile_a(k, std::true_type{}, [&]() __attribute__((always_inline)) { ring(k); });
+      __syncthreads();
+    }
+    __syncthreads();  // step nsteps: wave B's last tile
+  } else {
+    ring(0);
+    __syncthreads();
+    for (int k = 1; k <= nsteps; ++k) {
+      tile_b(k - 1, [&]() __attribute__((always_inline)) { ring(k); });
+      __syncthreads();
+    }
   }
 
-  // lane holds keys 16 c + 4 lg + i of the wave's 32, dims 16 m + li
-  uint16_t* const out = ROLE == 0 ? a.dV : a.dK;
-  const float osc = ROLE == 0 ? 1.f : a.scale;
+  // lane holds keys 16 c + 4 lg + i of the pair's 32, dims 16 m + li
+  uint16_t* const out = role_a ? a.dV : a.dK;
+  const float osc = role_a ? 1.f : a.scale;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = pair * kDkvKeys + wave * kDkvKeysPerWave + 16 * c + 4 * lg + i;
+      const int key = grp * kDkvKeys + pw * 32 + 16 * c + 4 * lg + i;
       if (key >= L) continue;
       const int64_t r = (static_cast<int64_t>(tok0 + key) * a.Hkv + g) * D;
 #pragma unroll
@@ -555,15 +665,13 @@ hipError_t launch_backward(const Shape& s, const Geometry& g, BwdArgs args, cons
   if (e != hipSuccess) return e;
   constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
   const unsigned grid = static_cast<unsigned>((args.max_items + span - 1) / span * span);
-  const dim3 dkv_grid(static_cast<unsigned>(dkv_items));
+  const dim3 dkv_grid(static_cast<unsigned>((dkv_items + span - 1) / span * span));
   if (s.d == 128) {
     hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<128, 0>), dkv_grid, dim3(kDkvThreads), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<128, 1>), dkv_grid, dim3(kDkvThreads), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128>), dkv_grid, dim3(kDkvThreads), 0, st, args);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(kAttnWaves * 64), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<64, 0>), dkv_grid, dim3(kDkvThreads), 0, st, args);
-    hipLaunchKernelGGL((bwd_dkv_kernel<64, 1>), dkv_grid, dim3(kDkvThreads), 0, st, args);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64>), dkv_grid, dim3(kDkvThreads), 0, st, args);
   }
   return hipGetLastError();
 }

@@ -322,9 +322,9 @@ struct BwdArgs {
   float scale;
 };
 
-// Keys per workgroup of the dK/dV kernels (32 per wave).
+// Keys per workgroup of the dK/dV kernel (32 per pair of waves).
 constexpr int kDkvWaves = 8;
-constexpr int kDkvKeys = 32 * kDkvWaves;
+constexpr int kDkvKeys = 16 * kDkvWaves;
 
 // Cost-ordered list of the dK/dV kernel's items (sequence, KV head, key
 // group), in its own workspace region.
