@@ -49,8 +49,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kXaThreads = 256;
+constexpr int kXaThreads = 512;
 constexpr int kXaWaves = kXaThreads / 64;
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// the wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt at their maxima, i.e. not waited for)
+constexpr int kReadsAhead = 6;  // B-operand reads in flight ahead of the MFMAs
+template <int N>
+constexpr int kVmcntAhead = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kMinusBig = -1.0e30f;
 // word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data, no swizzle)
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(kXaThreads) void xa_rows_kernel(const int8_t* __res
 }
 
 template <int D>
-__global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
+__global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
   constexpr int S = kXaStride;
   constexpr int KS = S * D / 32;                     // 32-wide k-steps of one group
   constexpr int KGS = S * D + 8;                     // elements per padded key group
@@ -176,43 +182,63 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
   constexpr int RPI = 1024 / (2 * D);                // key rows per 1 KiB load instruction
   constexpr int IPG = S / RPI;                       // load instructions per key group
   constexpr int NDMA = kXaBlock / RPI / kXaWaves;    // load instructions per wave per tile
+  constexpr int AHEAD = 3;                           // key tiles in flight beyond the one read
   static_assert(IPG >= 1 && IPG * RPI == S, "a key group is whole load instructions");
   static_assert(NDMA * RPI * kXaWaves == kXaBlock, "key tile must split evenly");
   static_assert(kXaGroupsPerBlock == 16, "one 16-row MFMA tile of groups per XA block");
+  static_assert(kXaWaves == 8, "two quads of waves, one per query block of the pair");
 
-  // two key tiles, each addressed only through its own name, so that the
-  // direct loads into one can be in flight while the other is read; the
-  // first doubles as the sort buffer once the scoring is done
-  __shared__ __attribute__((aligned(1024))) uint16_t Kt0[KT], Kt1[KT];
-  __shared__ float rlt[kXaWaves][kXaGroupsPerBlock];  // group-row totals of the quad's heads
+  // a ring of four key tiles, each addressed only through its own name, so
+  // that the direct loads into three of them can be in flight while the
+  // fourth is read; the first doubles as the sort buffer after the scoring
+  __shared__ __attribute__((aligned(1024))) uint16_t Kt0[KT], Kt1[KT], Kt2[KT], Kt3[KT];
+  __shared__ float rlt[kXaWaves][kXaGroupsPerBlock];  // group-row totals of the waves' (head, block)
   __shared__ float fz[2];                              // masses of the forced blocks
   __shared__ float redf[kXaWaves + 1];
   __shared__ int32_t redi[kXaWaves + 1];
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t* hm = reinterpret_cast<uint32_t*>(smem);    // [nqb] heads keeping block j
+  // [2][nqb]: heads keeping key block j, for the pair's upper and lower block
+  // (a group has at most 16 query heads)
+  uint16_t* hm2 = reinterpret_cast<uint16_t*>(smem);
   uint64_t* keys = reinterpret_cast<uint64_t*>(Kt0);
 
   // Work item t = the workgroup's position in the XCD-chunked order
-  // (list_position): items run in bands of kXcdChunk query blocks, the
-  // costliest (largest i) band first; inside a band, one XA row after the
-  // other, kXcdChunk consecutive query blocks each, so that the workgroups an
-  // XCD runs together stream the same key blocks through its L2.
+  // (list_position): a pair of query blocks (2 p + 1, 2 p) of one XA row;
+  // items run in bands of kXcdChunk pairs, the costliest (largest p) band
+  // first; inside a band, one XA row after the other, kXcdChunk consecutive
+  // pairs each, so that the workgroups an XCD runs together stream the same
+  // key blocks through its L2.
   const int64_t t = list_position(blockIdx.x);
   const int n_rows = a.meta[kMetaXaRows];
+  const int nqp = (a.nqb + 1) / 2;
   if (t >= static_cast<int64_t>(n_rows) * a.nqb_pad) return;
   const int64_t band = t / (static_cast<int64_t>(kXcdChunk) * n_rows);
   const int rem = static_cast<int>(t - band * kXcdChunk * n_rows);
   const int bk = a.rows[rem / kXcdChunk];
-  const int i = a.nqb_pad - 1 - static_cast<int>(band * kXcdChunk + rem % kXcdChunk);
+  const int pp = a.nqb_pad - 1 - static_cast<int>(band * kXcdChunk + rem % kXcdChunk);
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int tok0 = a.cu[b];
   const int L = a.cu[b + 1] - tok0;
-  if (i < 0 || i >= a.nqb || static_cast<int64_t>(i) * kXaBlock >= L) return;
+  if (pp < 0 || pp >= nqp) return;
+  // the pair's blocks: quad 0 takes 2 p + 1, quad 1 takes 2 p; a block past
+  // the sequence end (or past nqb) has no work
+  int ib[2];
+  bool bv[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    ib[q] = 2 * pp + 1 - q;
+    bv[q] = ib[q] < a.nqb && static_cast<int64_t>(ib[q]) * kXaBlock < L;
+  }
+  if (!bv[1]) return;  // then block 2 p + 1 lies past the end too
+  const int jmax = bv[0] ? ib[0] : ib[1];  // key blocks 0 .. jmax are walked
   const int ng = (L + S - 1) / S;  // position groups of the sequence
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int quad = wave / 4, wq = wave % 4;
+  const int i = ib[quad];         // this wave's query block
+  const bool iv = bv[quad];
   const int r = lane % 16, kq = lane / 16;
-  for (int j = tid; j <= i; j += kXaThreads) hm[j] = 0u;
+  for (int j = tid; j < 2 * a.nqb; j += kXaThreads) hm2[j] = 0;
 
   // Direct loads of key block j: instruction q = wave NDMA + n of the tile
   // fills rows (q % IPG) RPI .. + RPI - 1 of group q / IPG, lane l writing
@@ -230,12 +256,15 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
     dma_off[n] = ((q / IPG) * S + (q % IPG) * RPI + lane / (D / 8)) * rs2 + (lane % (D / 8)) * 16;
   }
   // (the offsets come in as a parameter: a lambda capturing a local array
-  // by reference makes the host pass drop this kernel's launch stub)
-  auto dma = [&](uint16_t* tile, int j, const int* off) {
-    const int key0 = j * kXaBlock;
+  // by reference makes the host pass drop this kernel's launch stub).  Key
+  // blocks past jmax load nothing, but every wave still counts NDMA loads per
+  // step: a block past the end reads the range-checked zero page.
+  auto dma = [&](uint16_t* tile, int j, const int* off) __attribute__((always_inline)) {
+    const int jj = min(j, jmax);
+    const int key0 = jj * kXaBlock;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kseq + static_cast<int64_t>(key0) * a.Hkv * D), 0,
-        static_cast<unsigned>(L - key0) * static_cast<unsigned>(rs2), kBufferWord3);
+        j <= jmax ? static_cast<unsigned>(L - key0) * static_cast<unsigned>(rs2) : 0u, kBufferWord3);
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) {
       const int q = wave * NDMA + n;
@@ -245,106 +274,153 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
     }
   };
 
-  for (int g0 = 0; g0 < a.G; g0 += kXaWaves) {
-    const int gg = g0 + wave;
-    const bool hv = gg < a.G;
-    const int hq = kvh * a.G + gg;
+  for (int g0 = 0; g0 < a.G; g0 += 4) {
+    const int gg = g0 + wq;
+    const bool hv = gg < a.G && iv;
+    const int hq = kvh * a.G + min(gg, a.G - 1);
     // A operand: group row 16 i + r, contraction index 32 kk + 8 kq + e =
     // t D + dim, i.e. query position (16 i + r) S + S-1-t
     bf16x8 qa[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const int t = (32 * kk) / D, dim = (32 * kk) % D + 8 * kq;
-      const int p = (16 * i + r) * S + S - 1 - t;
+      const int tt = (32 * kk) / D, dim = (32 * kk) % D + 8 * kq;
+      const int p = (16 * i + r) * S + S - 1 - tt;
       qa[kk] = (hv && p < L) ? *reinterpret_cast<const bf16x8*>(
                                    a.Q + (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + dim)
                              : bf16x8{};
     }
     // Lane holds group rows 16 i + 4 kq + e (e = 0..3), key group 16 j + r,
     // of each score tile.  Per key block: each row's log2-sum-exp2 over the
-    // block's 16 groups (a reduction over the 16 lanes of the row) goes to the
-    // workspace, and the row's running max and sum absorb it.
-    float M_e[4], L_e[4];
+    // block's 16 groups goes to the workspace and the row's running sum
+    // absorbs it.  The sums are taken against a running reference R of the
+    // row (uniform over its 16 lanes), not the block's own max: only when a
+    // sum passes 2^64 (or R is unset) does a rare branch take the block max,
+    // raise R and rescale the running sum.
+    float R_e[4], L_e[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      M_e[e] = kMinusBig;
+      R_e[e] = kMinusBig;
       L_e[e] = 0.f;
     }
     float* const lrow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hq) * xa_row_offset(a.nqb) +
                                  xa_row_offset(i)) * kXaGroupsPerBlock;
-    // block j from tile kt while block j + 1 loads into knext; the barrier at
-    // the end waits for that load and for every wave's reads of kt
-    auto step = [&](int j, const uint16_t* kt, uint16_t* knext) {
-      if (j < i) dma(knext, j + 1, dma_off);
-      if (hv) {
+    // step j: load block j + AHEAD into the tile block j - 1 used, score
+    // block j from kt, then wait for this wave's loads of block j + 1 (the
+    // AHEAD - 1 newer tiles may stay in flight) and meet the other waves
+    auto step = [&](int j, const uint16_t* kt, uint16_t* kload) __attribute__((always_inline)) {
+      dma(kload, j + AHEAD, dma_off);
+      if (hv && j <= i) {
         // B operand: key group column r (positions (16 j + r) S + t), same
         // k-slice: group r, row t, dims 32 kk % D + 8 kq, i.e. element
-        // r KGS + 32 kk + 8 kq; four independent accumulation chains keep
-        // the matrix pipe busy
-        f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+        // r KGS + 32 kk + 8 kq; two independent accumulation chains (a
+        // product's result is ready before its chain's next MFMA issues)
+        // The B-operand reads run kReadsAhead MFMAs ahead of their use,
+        // pinned there by scheduling fences (left alone, the compiler reads
+        // each one into the same registers right before its MFMA, which then
+        // waits out the whole LDS latency).
+        f32x4 sc[2] = {f32x4{}, f32x4{}};
+        bf16x8 kb[KS];
+        auto kread = [&](int kk) __attribute__((always_inline)) {
+          kb[kk] = *reinterpret_cast<const bf16x8*>(kt + r * KGS + 32 * kk + 8 * kq);
+        };
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          sc[kk & 3] = mfma16(qa[kk], *reinterpret_cast<const bf16x8*>(kt + r * KGS + 32 * kk + 8 * kq),
-                              sc[kk & 3]);
-        const f32x4 s = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+        for (int kk = 0; kk < kReadsAhead; ++kk) kread(kk);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          if (kk + kReadsAhead < KS) kread(kk + kReadsAhead);
+          __builtin_amdgcn_sched_barrier(0);
+          sc[kk & 1] = mfma16(qa[kk], kb[kk], sc[kk & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const f32x4 s = sc[0] + sc[1];
         const int c = 16 * j + r;  // this lane's key group
-        f32x4 blse;
+        f32x4 x, ps;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ag = 16 * i + 4 * kq + e;
-          const bool ok = c <= ag && ag < ng;
-          const float x = ok ? s[e] * a.cs : -INFINITY;
-          const float bm = row16_max(x);
-          const float ps = row16_sum(ok ? __builtin_amdgcn_exp2f(x - bm) : 0.f);
-          // an all-masked row of the block: bm = -inf, ps = 0, lse -inf, no change
-          blse[e] = bm + __log2f(ps);
-          const float mn = fmaxf(M_e[e], bm);
-          L_e[e] = L_e[e] * __builtin_amdgcn_exp2f(M_e[e] - mn) + ps * __builtin_amdgcn_exp2f(bm - mn);
-          M_e[e] = mn;
+          x[e] = (c <= ag && ag < ng) ? s[e] * a.cs : -INFINITY;
+          ps[e] = row16_sum(__builtin_amdgcn_exp2f(x[e] - R_e[e]));
+        }
+        const bool big = !(ps[0] <= 0x1p64f) || !(ps[1] <= 0x1p64f) || !(ps[2] <= 0x1p64f) ||
+                         !(ps[3] <= 0x1p64f);
+        if (__builtin_expect(__ballot(big) != 0, 0)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float rn = fmaxf(R_e[e], row16_max(x[e]));
+            L_e[e] *= __builtin_amdgcn_exp2f(R_e[e] - rn);
+            R_e[e] = rn;
+            ps[e] = row16_sum(__builtin_amdgcn_exp2f(x[e] - rn));
+          }
+        }
+        f32x4 blse;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // an all-masked row of the block: ps = 0, lse -inf, no change
+          blse[e] = R_e[e] + __log2f(ps[e]);
+          L_e[e] += ps[e];
         }
         if (r == 0) *reinterpret_cast<f32x4*>(lrow + j * kXaGroupsPerBlock + 4 * kq) = blse;
       }
-      __syncthreads();
+      // this wave's loads of block j + 1 are done once at most the loads of
+      // the AHEAD - 1 tiles after it are outstanding.  Then the barrier, which
+      // the compiler may move no memory access across (a fence would also wait
+      // for the loads still meant to be in flight).
+      __builtin_amdgcn_s_waitcnt(kVmcntAhead<NDMA * (AHEAD - 1)>);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
     dma(Kt0, 0, dma_off);
+    dma(Kt1, 1, dma_off);
+    dma(Kt2, 2, dma_off);
+    __builtin_amdgcn_s_waitcnt(kVmcntAhead<NDMA * (AHEAD - 1)>);
     __syncthreads();
-    for (int j = 0; j <= i; j += 2) {
-      step(j, Kt0, Kt1);
-      if (j + 1 <= i) step(j + 1, Kt1, Kt0);
+    for (int j = 0; j <= jmax; j += 4) {
+      step(j, Kt0, Kt3);
+      if (j + 1 <= jmax) step(j + 1, Kt1, Kt0);
+      if (j + 2 <= jmax) step(j + 2, Kt2, Kt1);
+      if (j + 3 <= jmax) step(j + 3, Kt3, Kt2);
     }
-    // the quad's group-row totals (uniform over the 16 lanes of a row)
+    // no load may still be writing a tile when the first one becomes the
+    // sort buffer
+    __builtin_amdgcn_s_waitcnt(kVmcntAhead<0>);
+    // the group-row totals (uniform over the 16 lanes of a row)
     if (hv && r == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rlt[wave][4 * kq + e] = M_e[e] + __log2f(L_e[e]);
+      for (int e = 0; e < 4; ++e) rlt[wave][4 * kq + e] = R_e[e] + __log2f(L_e[e]);
     }
     __syncthreads();  // totals and workspace rows written; the key tiles are free
 
-    // Threshold selection of each head of the quad, the whole workgroup at a
-    // time.  Block masses A[i][j] = sum over the group rows (those before the
-    // sequence's last group) of 2^(block lse - row total).
-    for (int w = 0; w < kXaWaves && g0 + w < a.G; ++w) {
-      const int hqw = kvh * a.G + g0 + w;
+    // Threshold selection of each (head, block) of the two quads, the whole
+    // workgroup at a time.  Block masses A[i][j] = sum over the group rows
+    // (those before the sequence's last group) of 2^(block lse - row total).
+    for (int w = 0; w < kXaWaves; ++w) {
+      const int qd = w / 4, gw = g0 + w % 4;
+      if (gw >= a.G || !bv[qd]) continue;  // workgroup-uniform
+      const int iw = ib[qd];
+      uint16_t* hm = hm2 + qd * a.nqb;
+      const int hqw = kvh * a.G + gw;
       const float* srow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hqw) * xa_row_offset(a.nqb) +
-                                   xa_row_offset(i)) * kXaGroupsPerBlock;
-      const uint32_t bit = 1u << (g0 + w);
-      const int m = i - 1;  // candidates: blocks 1 .. i-1
+                                   xa_row_offset(iw)) * kXaGroupsPerBlock;
+      const uint16_t bit = static_cast<uint16_t>(1u << gw);
+      const int m = iw - 1;  // candidates: blocks 1 .. iw-1
       int P2 = 1;
       while (P2 < m) P2 <<= 1;
       float part = 0.f;
-      for (int j = tid; j <= i; j += kXaThreads) {
+      for (int j = tid; j <= iw; j += kXaThreads) {
         float mj = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(srow + j * kXaGroupsPerBlock + 4 * q);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (16 * i + 4 * q + e < ng) mj += __builtin_amdgcn_exp2f(v[e] - rlt[w][4 * q + e]);
+            if (16 * iw + 4 * q + e < ng) mj += __builtin_amdgcn_exp2f(v[e] - rlt[w][4 * q + e]);
         }
         part += mj;
-        if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + i) * a.nqb + j] = mj;
+        if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb + j] = mj;
         if (j == 0) fz[0] = mj;
-        if (j == i) fz[1] = mj;
-        if (j >= 1 && j < i)
+        if (j == iw) fz[1] = mj;
+        if (j >= 1 && j < iw)
           keys[j - 1] = (static_cast<uint64_t>(__float_as_uint(mj)) << 32) |
                         static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(j));
       }
@@ -352,7 +428,7 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
         if (p >= 0) keys[p] = 0ull;
       const float total = block_sum(part, redf);  // its barriers publish keys and fz
       const float target = a.tau * total;
-      const float forced = i > 0 ? fz[0] + fz[1] : fz[0];
+      const float forced = iw > 0 ? fz[0] + fz[1] : fz[0];
       if (m > 0) {
         // bitonic sort, descending
         for (int k = 2; k <= P2; k <<= 1) {
@@ -390,29 +466,36 @@ __global__ __launch_bounds__(kXaThreads, 2) void xa_plan_kernel(XaArgs a) {
       }
       if (tid == 0) {
         hm[0] |= bit;
-        hm[i] |= bit;
+        hm[iw] |= bit;
       }
       __syncthreads();
       if (a.keep) {
-        uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + i) * a.nqb;
-        for (int j = tid; j <= i; j += kXaThreads) krow[j] = (hm[j] & bit) ? 1 : 0;
+        uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb;
+        for (int j = tid; j <= iw; j += kXaThreads) krow[j] = (hm[j] & bit) ? 1 : 0;
       }
     }
     __syncthreads();  // the sort buffer (first key tile) is free again
   }
 
-  // Ascending list of the key blocks some head of the group keeps.
-  const int per = (i + 1 + kXaThreads - 1) / kXaThreads;
-  const int j0 = tid * per;
-  int32_t mine = 0;
-  for (int j = j0; j < min(j0 + per, i + 1); ++j) mine += hm[j] != 0u;
-  int32_t count;
-  int32_t pos = block_exclusive(mine, redi, &count);
-  int32_t* lrow = a.list + static_cast<int64_t>(bk) * xa_row_offset(a.nqb) + xa_row_offset(i);
-  for (int j = j0; j < min(j0 + per, i + 1); ++j) {
-    if (hm[j] != 0u) lrow[pos++] = j | static_cast<int32_t>(hm[j] << 16);
+  // Ascending list of the key blocks some head of the group keeps, for each
+  // block of the pair.
+  for (int qd = 0; qd < 2; ++qd) {
+    if (!bv[qd]) continue;  // workgroup-uniform
+    const int iw = ib[qd];
+    const uint16_t* hm = hm2 + qd * a.nqb;
+    const int per = (iw + 1 + kXaThreads - 1) / kXaThreads;
+    const int j0 = tid * per;
+    int32_t mine = 0;
+    for (int j = j0; j < min(j0 + per, iw + 1); ++j) mine += hm[j] != 0;
+    int32_t count;
+    int32_t pos = block_exclusive(mine, redi, &count);
+    int32_t* lrow = a.list + static_cast<int64_t>(bk) * xa_row_offset(a.nqb) + xa_row_offset(iw);
+    for (int j = j0; j < min(j0 + per, iw + 1); ++j) {
+      if (hm[j] != 0) lrow[pos++] = j | (static_cast<int32_t>(hm[j]) << 16);
+    }
+    if (tid == 0) a.cnt[static_cast<int64_t>(bk) * a.nqb + iw] = count;
+    __syncthreads();  // redi is reused by the next block's prefix
   }
-  if (tid == 0) a.cnt[static_cast<int64_t>(bk) * a.nqb + i] = count;
 }
 
 }  // namespace
@@ -424,7 +507,7 @@ size_t xa_plan_lds_bytes(const Shape& s) {
   // the sort keys of one query block reuse the first key tile
   const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + 8) * 2;
   if (nqb > 4096 || 8u * static_cast<size_t>(P2) > ktile) return 0;
-  return sizeof(uint32_t) * static_cast<size_t>(nqb);
+  return 2 * sizeof(uint16_t) * static_cast<size_t>(nqb);
 }
 
 hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const void* Q,
@@ -450,7 +533,8 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   a.Hkv = s.Hkv;
   a.G = s.G;
   a.nqb = ws.xa_nqb;
-  a.nqb_pad = (ws.xa_nqb + kXcdChunk - 1) / kXcdChunk * kXcdChunk;
+  // pairs of query blocks, in whole bands of kXcdChunk
+  a.nqb_pad = ((ws.xa_nqb + 1) / 2 + kXcdChunk - 1) / kXcdChunk * kXcdChunk;
   a.head_config = s.head_config;
   a.cs = g.scale * kLog2e / kXaStride;
   a.tau = tau;
@@ -458,8 +542,8 @@ hipError_t launch_xa_plan(const Shape& s, const Geometry& g, float tau, const vo
   if (lds == 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(xa_rows_kernel, dim3(1), dim3(kXaThreads), 0, st, modes, cu, s.B, s.Hkv,
                      s.head_config, rows, meta);
-  // one workgroup per (XA row, query block) at most, rounded up to whole
-  // rounds of the XCD-chunked order
+  // one workgroup per (XA row, pair of query blocks) at most, rounded up to
+  // whole rounds of the XCD-chunked order
   constexpr int64_t span = static_cast<int64_t>(kNumXcd) * kXcdChunk;
   const int64_t items = static_cast<int64_t>(a.nqb_pad) * s.B * s.Hkv;
   const unsigned grid = static_cast<unsigned>((items + span - 1) / span * span);
