@@ -25,7 +25,6 @@
 
 #include <type_traits>
 
-
 namespace ea {
 namespace {
 
@@ -366,25 +365,42 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
     for (int m = 0; m < NM; ++m) acc[c][m] = f32x4{};
   const float cl = a.scale * kLog2e;
 
-  // tile t -> registers -> ring buffer
+  // tile t -> registers -> ring buffer.  Buffer loads: a resource per tile
+  // (uniform) whose range ends at the sequence end, so rows past it read as
+  // zeros without a branch, and per-thread offsets that stay the same from
+  // tile to tile.
   u32x4 qreg[NCH], oreg[NCH];
   float lreg = 0.f, dreg = 0.f;
+  int toff[NCH];  // byte offset of this thread's chunks inside a tile's rows
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+    toff[k] = (r * a.Hq * D + col) * 2;
+  }
   auto fetch = [&](int t) __attribute__((always_inline)) {
     const int qb = qb_hi - t / a.G;
     const int hq = g * a.G + t % a.G;
+    const int rows = L - qb * kBlock;  // > 0: qb is a block of the sequence
+    const int64_t row0 = (static_cast<int64_t>(tok0) + qb * kBlock) * a.Hq + hq;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.Q + row0 * D), 0, static_cast<unsigned>(rows) * a.Hq * D * 2u, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.dO + row0 * D), 0, static_cast<unsigned>(rows) * a.Hq * D * 2u, kBufferWord3);
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const int ci = k * kDkvThreads + tid, r = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      const int p = qb * kBlock + r;
-      const int64_t src = (static_cast<int64_t>(tok0 + p) * a.Hq + hq) * D + col;
-      qreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.Q + src) : u32x4{0, 0, 0, 0};
-      oreg[k] = p < L ? *reinterpret_cast<const u32x4*>(a.dO + src) : u32x4{0, 0, 0, 0};
+      qreg[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, toff[k], 0, 0));
+      oreg[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, toff[k], 0, 0));
     }
     if (tid < kBlock) {
-      const int p = qb * kBlock + tid;
-      const int64_t ix = static_cast<int64_t>(hq) * a.T + tok0 + p;
-      lreg = p < L ? a.lse2[ix] : INFINITY;
-      dreg = p < L ? a.Dv[ix] : 0.f;
+      const int64_t ix = static_cast<int64_t>(hq) * a.T + tok0 + qb * kBlock;
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.lse2 + ix), 0, static_cast<unsigned>(rows) * 4u, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.Dv + ix), 0, static_cast<unsigned>(rows) * 4u, kBufferWord3);
+      lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0));
+      dreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+      // a row past the end: LSE +inf, so that its P is 0 (its Q and dO are 0)
+      if (tid >= rows) lreg = INFINITY;
     }
   };
   auto stage = [&](int t) __attribute__((always_inline)) {
