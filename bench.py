@@ -31,6 +31,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import re
 import json
 import os
 import platform
@@ -46,8 +47,9 @@ if ROOT not in sys.path:
 METRIC = "hybrid prefill effective TFLOP/s + ms/layer at 128K; % bf16 MFMA roofline"
 DEFAULT_RUNS = ["qwen4b_s128k_sa2", "qwen4b_s128k_sa6"]
 # The sources that decide the attention kernel's memory traffic: the kernel,
-# the work-list order that places its workgroups on the XCDs, and the tiling
-# constants of the shared header.
+# the work-list order that places its workgroups on the XCDs, and the
+# constants of the shared header that those two use (with the constants their
+# definitions use in turn).
 ATTN_SRCS = [os.path.join(ROOT, "full_attention_long_amd", "csrc", f)
              for f in ("ea_attention.hip", "ea_worklist.hip")]
 ATTN_HEADER = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_internal.h")
@@ -95,12 +97,28 @@ def mfma_probe(target_ms: float = 100.0, launches: int = 3) -> dict:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
+    texts = []
     for path in ATTN_SRCS:
         with open(path, "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        h.update(data)
+        texts.append(data.decode())
+    defs, code = {}, []
     with open(ATTN_HEADER) as f:
-        consts = [ln.strip() for ln in f if ln.strip().startswith("constexpr int k")]
-    h.update("\n".join(consts).encode())
+        for ln in f:
+            m = re.match(r"\s*constexpr int (k\w+)\s*=", ln)
+            if m:
+                defs[m.group(1)] = ln.strip()
+            else:
+                code.append(ln.split("//")[0])  # the header's own code (its helpers)
+    used, todo = set(), "\n".join(texts + code)
+    while True:
+        new = {k for k in defs if k not in used and re.search(r"\b%s\b" % k, todo)}
+        if not new:
+            break
+        used |= new
+        todo = "\n".join(defs[k] for k in new)
+    h.update("\n".join(defs[k] for k in sorted(used)).encode())
     return h.hexdigest()[:16]
 
 
