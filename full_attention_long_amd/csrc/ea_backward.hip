@@ -314,19 +314,24 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   // raw item ((b Hkv + g) npair + grp), taken in the list's cost order, in
   // chunks of consecutive entries per XCD: within a cost band the list holds
   // the key chunks of one head in a row, so those share the XCD's cache
+  // The item's values are the same for the whole workgroup; they are read
+  // with vector loads (the kernel writes global memory, so the compiler cannot
+  // read them as constants) and made scalar by readfirstlane, so that every
+  // tile address and buffer resource derived from them stays in SGPRs.
+  auto uni = [](int v) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(v); };
   const int64_t pos = list_position(blockIdx.x);
   if (pos >= a.dkv_n) return;
-  const int64_t item = a.dkv_order[pos];
+  const int64_t item = uni(a.dkv_order[pos]);
   const int grp = static_cast<int>(item % a.npair);
   const int64_t rest = item / a.npair;
   const int g = static_cast<int>(rest % a.Hkv);
   const int b = static_cast<int>(rest / a.Hkv);
-  if (a.meta[kMetaStamp] != a.stamp) return;  // the planner rejected the device contents
-  const int tok0 = a.cu[b];
-  const int L = a.cu[b + 1] - tok0;
+  if (uni(a.meta[kMetaStamp]) != a.stamp) return;  // the planner rejected the device contents
+  const int tok0 = uni(a.cu[b]);
+  const int L = uni(a.cu[b + 1]) - tok0;
   if (grp * kDkvKeys >= L) return;
-  const int mode = a.modes[static_cast<int64_t>(b) * a.Hkv + g] != 0 ? kModeSA : kModeFA;
-  const int ns = a.n_sink, w = a.seq_w[b];
+  const int mode = uni(a.modes[static_cast<int64_t>(b) * a.Hkv + g]) != 0 ? kModeSA : kModeFA;
+  const int ns = a.n_sink, w = uni(a.seq_w[b]);
   const int N = (L + kBlock - 1) / kBlock;
   const int kb0 = grp * (kDkvKeys / kBlock);
   const int kb1 = min(N - 1, kb0 + kDkvKeys / kBlock - 1);
@@ -338,13 +343,13 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   const int lane = tid % 64, lg = lane / 16, li = lane % 16;
   const bool role_a = wave < kDkvPairs;  // wave-uniform
   const int pw = wave % kDkvPairs;       // the pair, and its 32 keys
-  // this lane's key of key tile c as a B column, and its block
-  int key_b[2], kbj[2];
+  // this lane's key of key tile c as a B column; the pair's 32 keys lie in
+  // one 64-key block, kbj (computed from wave-uniform values, so that the
+  // loop bounds derived from it stay scalar)
+  int key_b[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    key_b[c] = grp * kDkvKeys + pw * 32 + 16 * c + li;
-    kbj[c] = key_b[c] / kBlock;
-  }
+  for (int c = 0; c < 2; ++c) key_b[c] = grp * kDkvKeys + pw * 32 + 16 * c + li;
+  const int kbj = (grp * kDkvKeys + pw * 32) / kBlock;
   // K (wave A) or V (wave B) rows as the B operands of S = Q K^T or dP = dO V^T
   bf16x8 bfr[2][NU];
   {
@@ -498,7 +503,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
             if constexpr (MASKED) {
               const int p = qb * kBlock + 16 * qt + 4 * lg + i;
               const bool vis = key_b[c] <= p && p < L &&
-                               (mode == kModeFA || kbj[c] < ns || p / kBlock - kbj[c] < w);
+                               (mode == kModeFA || kbj < ns || p / kBlock - kbj < w);
               e = vis ? e : -INFINITY;
             }
             pa[c][4 * t2 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(e));
@@ -580,8 +585,8 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
     // down, so a middle range of k) take the unmasked variant; each variant
     // runs in a loop of its own, so each is register-allocated alone.
     int qf = L / kBlock - 1;
-    if (mode == kModeSA && kbj[0] >= ns) qf = min(qf, kbj[0] + w - 1);
-    const int m1 = min(nsteps, max(0, (qb_hi - kbj[0]) * a.G));
+    if (mode == kModeSA && kbj >= ns) qf = min(qf, kbj + w - 1);
+    const int m1 = min(nsteps, max(0, (qb_hi - kbj) * a.G));
     const int m0 = min(m1, max(0, (qb_hi - qf) * a.G));
     int k = 0;
     for (; k < m0; ++k) {
