@@ -434,12 +434,17 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   // hides behind other work.
   typedef bf16x8 RowOps[2][NU];
   typedef bf16x8 ColOps[NM];
+  // this lane's part of each read's LDS address, formed once: every read of
+  // a step is then one tile base plus this plus a constant
+  const int row_lane = li * QROW + 8 * lg;
+  const int col_lane = (4 * lg + li / 4) * QROW + 4 * (li & 3);
   auto load_rows = [&](const uint16_t* src, int hf, RowOps& qa) __attribute__((always_inline)) {
+    const uint16_t* base = src + row_lane;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int u = 0; u < NU; ++u)
-        qa[t2][u] = *reinterpret_cast<const bf16x8*>(src + (16 * (2 * hf + t2) + li) * QROW + 32 * u + 8 * lg);
+        qa[t2][u] = *reinterpret_cast<const bf16x8*>(base + 16 * (2 * hf + t2) * QROW + 32 * u);
   };
   auto mma_rows = [&](const RowOps& qa, f32x4 (*x)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -452,12 +457,17 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
         for (int c = 0; c < 2; ++c) x[t2][c] = mfma16(qa[t2][u], bfr[c][u], x[t2][c]);
     }
   };
-  auto load_cols = [&](const uint16_t* src, int hf, ColOps& bt) __attribute__((always_inline)) {
+  // (tile = ring slot 2 buf + tensor; the lane's offset into it goes through
+  // an empty asm so that it stays one register and each read's constant part
+  // folds into the instruction's offset field, where the compiler would
+  // otherwise keep 16 per-read lane offsets and add the slot to each)
+  auto load_cols = [&](int tile, int hf, ColOps& bt) __attribute__((always_inline)) {
+    int off = tile * TILE + col_lane;
+    asm("" : "+v"(off));
+    const uint16_t* base = &Ts[0][0][0] + off;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int off = (32 * hf + 4 * lg + li / 4) * QROW + 16 * m + 4 * (li & 3);
-      bt[m] = tr_pair(src + off, src + off + 16 * QROW);
-    }
+    for (int m = 0; m < NM; ++m)
+      bt[m] = tr_pair(base + 32 * hf * QROW + 16 * m, base + (32 * hf + 16) * QROW + 16 * m);
   };
   // m in [m0, m1)
   auto mma_cols = [&](const bf16x8* xa, const ColOps& bt, int m0, int m1) __attribute__((always_inline)) {
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
       fence();
       mma_rows(qa, s);
       fence();
-      load_cols(Ot, hf, bt);
+      load_cols(2 * (t % 3) + 1, hf, bt);
       fence();
       bf16x8 pa[2];
 #pragma unroll
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
       fence();
       mma_rows(qa, dp);
       fence();
-      load_cols(Qt, hf, bt);
+      load_cols(2 * (t % 3), hf, bt);
       bf16x8 pa[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) pa[c] = Px[t & 1][pw][2 * hf + c][lane];
