@@ -176,10 +176,13 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) toff[t] = vr * D + (4 * (t ^ j) + clow) * 8 + 4 * (lane & 1);
   }
-  // A-operand rows of a row-layout tile times the B fragments
-  auto rowmm = [&](const uint16_t* tile, const bf16x8* bf, f32x16& x0, f32x16& x1) {
-    x0 = f32x16{};
-    x1 = f32x16{};
+  // A-operand rows of a row-layout tile times the B fragments, added to init
+  auto rowmm = [&](const uint16_t* tile, const bf16x8* bf, f32x16& x0, f32x16& x1, float init) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x0[e] = init;
+      x1[e] = init;
+    }
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int o0 = ((u & 1) ? koff_o : koff_e) + 16 * u;
@@ -194,10 +197,16 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 
   auto block = [&](int kb, const uint16_t* kr_, const uint16_t* vr_, const uint16_t* kt_) {
     f32x16 s0, s1, p0v, p1v;
-    rowmm(kr_, qf, s0, s1);
+    rowmm(kr_, qf, s0, s1, 0.f);
     // dP^T needs only LDS operands: issued here, its products run in the
     // matrix pipe while the exponentials below wait on and consume S
-    rowmm(vr_, of, p0v, p1v);
+    // dP^T - D straight from the products (the accumulators start at -D; the
+    // start value passes through an empty asm so that its 32 broadcast
+    // registers are set here rather than hoisted out of the block loop):
+    // 32 subtractions per block become 16 register moves
+    float nd = -drow;
+    asm volatile("" : "+v"(nd));
+    rowmm(vr_, of, p0v, p1v, nd);
     // a block every row of the tile sees (the common case) skips the
     // per-element visibility test
     if (block_full(mode, kb, p0, qb0, qb1, ns, w)) {
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int k = 8 * (q & 1) + e;
-        t[e] = q < 2 ? s0[k] * (p0v[k] - drow) : s1[k] * (p1v[k] - drow);
+        t[e] = q < 2 ? s0[k] * p0v[k] : s1[k] * p1v[k];
       }
       dsb[q] = __builtin_convertvector(t, bf16x8);
     }
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int TILE = kBlock * QROW;
   constexpr int NCH = kBlock * D / 8 / kDkvThreads;  // 16-byte chunks per thread per tile
   static_assert(NCH * kDkvThreads * 8 == kBlock * D, "tile must split evenly");
-  // ring of 3 tiles: [buffer][Q, dO] rows, [buffer][LSE, D]
+  // ring of 3 tiles: [buffer][Q, dO] rows, [buffer][LSE, -D]
   __shared__ __attribute__((aligned(16))) uint16_t Ts[3][2][TILE];
   __shared__ __attribute__((aligned(16))) float Ls[3][2][kBlock];
   // P of each pair as bf16 A operands: [tile parity][pair][2 half + key tile][lane]
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
     }
     if (tid < kBlock) {
       Ls[buf][0][tid] = lreg;
-      Ls[buf][1][tid] = dreg;
+      Ls[buf][1][tid] = -dreg;
     }
   };
 
@@ -446,11 +455,11 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
       for (int u = 0; u < NU; ++u)
         qa[t2][u] = *reinterpret_cast<const bf16x8*>(base + 16 * (2 * hf + t2) * QROW + 32 * u);
   };
-  auto mma_rows = [&](const RowOps& qa, f32x4 (*x)[2]) __attribute__((always_inline)) {
+  auto mma_rows = [&](const RowOps& qa, f32x4 (*x)[2], const f32x4* init) __attribute__((always_inline)) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) x[t2][c] = f32x4{};
+      for (int c = 0; c < 2; ++c) x[t2][c] = init ? init[t2] : f32x4{};
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
     for (int hf = 0; hf < 2; ++hf) {
       f32x4 s[2][2];
       fence();
-      mma_rows(qa, s);
+      mma_rows(qa, s, nullptr);
       fence();
       load_cols(2 * (t % 3) + 1, hf, bt);
       fence();
@@ -540,19 +549,24 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
     RowOps qa;
     ColOps bt;
     load_rows(Ot, 0, qa);
+    // -D of the tile's rows (the ring holds D negated): the dP accumulators
+    // start there, so the products give dP - D (16 subtractions per half
+    // fewer)
+    f32x4 nd[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) nd[hf][t2] = *reinterpret_cast<const f32x4*>(Dt + 16 * (2 * hf + t2) + 4 * lg);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       f32x4 dp[2][2];
       fence();
-      mma_rows(qa, dp);
+      mma_rows(qa, dp, nd[hf]);
       fence();
       load_cols(2 * (t % 3), hf, bt);
       bf16x8 pa[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) pa[c] = Px[t & 1][pw][2 * hf + c][lane];
-      f32x4 dv4[2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) dv4[t2] = *reinterpret_cast<const f32x4*>(Dt + 16 * (2 * hf + t2) + 4 * lg);
       fence();
       bf16x8 ds[2];
 #pragma unroll
@@ -561,8 +575,7 @@ __global__ __launch_bounds__(kDkvThreads) void bwd_dkv_kernel(BwdArgs a) {
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            ds[c][4 * t2 + i] =
-                static_cast<__bf16>(static_cast<float>(pa[c][4 * t2 + i]) * (dp[t2][c][i] - dv4[t2][i]));
+            ds[c][4 * t2 + i] = static_cast<__bf16>(static_cast<float>(pa[c][4 * t2 + i]) * dp[t2][c][i]);
       fence();
       mma_cols(ds, bt, 0, NM / 2);
       fence();
