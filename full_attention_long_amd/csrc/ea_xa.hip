@@ -17,20 +17,21 @@
 //                 to the lower index) until the kept mass reaches tau times
 //                 the row total.
 //
-// One workgroup per (sequence, KV head, XA query block i), 4 waves, the KV
-// group's query heads taken 4 at a time (one per wave).  A wave keeps its
-// head's 16 group rows of block i in registers as the A operand of
-// 16x16x32 bf16 MFMAs: the contraction runs over the S * d values of a group
-// (S query rows in reversed order, d dims each), so one 16 x 16 tile of group
-// scores is S d / 32 MFMAs.  Key blocks j = 0..i stream through LDS (128 key
-// rows, the 8 rows of each group contiguous and groups padded by 16 bytes, so
-// that the 16 columns of a B operand read start on distinct bank groups and
-// every read is one base register plus an immediate offset), staged through
-// registers one block ahead.  The key blocks are walked once: per block, each
-// group row's log2-sum-exp2 over the block's 16 groups (DPP reductions over
-// the 16 lanes of the row) goes to the workspace and updates the row's running
-// total; once the totals are known, A[i][j] = sum over the rows of
-// 2^(block lse - row total).
+// One workgroup of 8 waves per (sequence, KV head, pair of XA query blocks
+// 2p + 1 and 2p): waves 0-3 score block 2p + 1, waves 4-7 block 2p, for the
+// KV group's query heads 4 at a time (one per wave).  A wave keeps its head's
+// 16 group rows of its block in registers as the A operand of 16x16x32 bf16
+// MFMAs: the contraction runs over the S * d values of a group (S query rows
+// in reversed order, d dims each), so one 16 x 16 tile of group scores is
+// S d / 32 MFMAs.  Key blocks j = 0..2p + 1 stream through LDS once for both
+// blocks (128 key rows, the 8 rows of each group contiguous and groups padded
+// by 32 bytes, so that the B-operand reads are free of bank conflicts and
+// every read is one base register plus an immediate offset), by direct
+// buffer-to-LDS loads into a ring of four tiles three blocks ahead.  Per key
+// block, each group row's log2-sum-exp2 over the block's 16 groups (DPP
+// reductions over the 16 lanes of the row) goes to the workspace and updates
+// the row's running total; once the totals are known, A[i][j] = sum over the
+// rows of 2^(block lse - row total).
 // The selection then runs in the same workgroup over its LDS row of masses: a
 // bitonic sort of the candidates (mass bits above the inverted block index,
 // so equal masses keep ascending index), a prefix sum in sorted order and the
@@ -50,6 +51,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXaThreads = 512;
+// elements of padding after each 8-row key group in the LDS key tiles
+constexpr int kXaGroupPad = 16;
 constexpr int kXaWaves = kXaThreads / 64;
 // s_waitcnt immediate that waits until at most N vector-memory operations of
 // the wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
@@ -177,7 +180,7 @@ template <int D>
 __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
   constexpr int S = kXaStride;
   constexpr int KS = S * D / 32;                     // 32-wide k-steps of one group
-  constexpr int KGS = S * D + 8;                     // elements per padded key group
+  constexpr int KGS = S * D + kXaGroupPad;           // elements per padded key group
   constexpr int KT = kXaGroupsPerBlock * KGS;        // elements of one key tile
   constexpr int RPI = 1024 / (2 * D);                // key rows per 1 KiB load instruction
   constexpr int IPG = S / RPI;                       // load instructions per key group
@@ -245,8 +248,12 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
   // 16-byte chunk l % (D / 8) of row l / (D / 8).  The buffer resource ends at
   // the sequence end (rows past it read as zeros; the whole offset is in the
   // range-checked vector offset).  LDS: the 8 rows of a group contiguous,
-  // groups padded by 16 bytes, so the 16 groups a B-operand read touches start
-  // on 16 distinct 16-byte bank groups.
+  // groups padded by 32 bytes (an odd multiple of 32 bytes apart): a B-operand
+  // read's lanes r and kq (groups r, 16-byte column kq) then land on distinct
+  // 16-byte bank groups within each set of lanes the LDS serves together (with
+  // 16-byte padding, lanes of adjacent kq collided: the bank-conflict counter
+  // read 28% of the kernel's time, and the selection took 10.0 ms instead of
+  // 8.1 at 128K).
   const int rs2 = a.Hkv * D * 2;  // bytes between key rows
   const uint16_t* kseq = a.K + (static_cast<int64_t>(tok0) * a.Hkv + kvh) * D;
   int dma_off[NDMA];
@@ -505,7 +512,7 @@ size_t xa_plan_lds_bytes(const Shape& s) {
   int P2 = 1;
   while (P2 < nqb) P2 <<= 1;
   // the sort keys of one query block reuse the first key tile
-  const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + 8) * 2;
+  const size_t ktile = static_cast<size_t>(kXaGroupsPerBlock) * (kXaStride * s.d + kXaGroupPad) * 2;
   if (nqb > 4096 || 8u * static_cast<size_t>(P2) > ktile) return 0;
   return 2 * sizeof(uint16_t) * static_cast<size_t>(nqb);
 }
