@@ -32,9 +32,10 @@
 // reductions over the 16 lanes of the row) goes to the workspace and updates
 // the row's running total; once the totals are known, A[i][j] = sum over the
 // rows of 2^(block lse - row total).
-// The selection then runs in the same workgroup over its LDS row of masses: a
-// bitonic sort of the candidates (mass bits above the inverted block index,
-// so equal masses keep ascending index), a prefix sum in sorted order and the
+// The selection then runs in the same workgroup, a wave per (head, block)
+// row: the row's masses, a bitonic sort of its candidates (mass bits above
+// the inverted block index, so equal masses keep ascending index; the rows'
+// sorts share one pass of barriers), a prefix sum in sorted order and the
 // threshold test in float32.  The per-head keep flags of the KV group are
 // OR-ed into one mask per key block, and the kept blocks are written as one
 // ascending list of (j | head mask << 16) for the attention kernel, which
@@ -115,18 +116,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum of one value per thread over the workgroup (red: kXaWaves floats).
-__device__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kXaWaves; ++w) s += red[w];
-  return s;
-}
-
 // Exclusive prefix over the workgroup of one value per thread, in thread
 // order (red: kXaWaves + 1 floats); returns the prefix, *total the sum.
 template <typename T>
@@ -193,17 +182,14 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
 
   // a ring of four key tiles, each addressed only through its own name, so
   // that the direct loads into three of them can be in flight while the
-  // fourth is read; the first doubles as the sort buffer after the scoring
+  // fourth is read; after the scoring they hold the selection's sort keys
   __shared__ __attribute__((aligned(1024))) uint16_t Kt0[KT], Kt1[KT], Kt2[KT], Kt3[KT];
   __shared__ float rlt[kXaWaves][kXaGroupsPerBlock];  // group-row totals of the waves' (head, block)
-  __shared__ float fz[2];                              // masses of the forced blocks
-  __shared__ float redf[kXaWaves + 1];
   __shared__ int32_t redi[kXaWaves + 1];
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // [2][nqb]: heads keeping key block j, for the pair's upper and lower block
   // (a group has at most 16 query heads)
   uint16_t* hm2 = reinterpret_cast<uint16_t*>(smem);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(Kt0);
 
   // Work item t = the workgroup's position in the XCD-chunked order
   // (list_position): a pair of query blocks (2 p + 1, 2 p) of one XA row;
@@ -398,90 +384,122 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
     }
     __syncthreads();  // totals and workspace rows written; the key tiles are free
 
-    // Threshold selection of each (head, block) of the two quads, the whole
-    // workgroup at a time.  Block masses A[i][j] = sum over the group rows
-    // (those before the sequence's last group) of 2^(block lse - row total).
-    for (int w = 0; w < kXaWaves; ++w) {
-      const int qd = w / 4, gw = g0 + w % 4;
-      if (gw >= a.G || !bv[qd]) continue;  // workgroup-uniform
-      const int iw = ib[qd];
-      uint16_t* hm = hm2 + qd * a.nqb;
-      const int hqw = kvh * a.G + gw;
-      const float* srow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hqw) * xa_row_offset(a.nqb) +
-                                   xa_row_offset(iw)) * kXaGroupsPerBlock;
-      const uint16_t bit = static_cast<uint16_t>(1u << gw);
-      const int m = iw - 1;  // candidates: blocks 1 .. iw-1
+    // Threshold selection of the (head, block) rows of the two quads, row w =
+    // (block of quad w / 4, head g0 + w % 4), wave w taking row w.  Block
+    // masses A[i][j] = sum over the group rows (those before the sequence's
+    // last group) of 2^(block lse - row total).  Each wave forms its row's
+    // masses and sort keys; one bitonic sort over the whole workgroup then
+    // orders the keys of up to 8 rows at once (a barrier per stage for all of
+    // them rather than per row), and each wave takes its row's prefix sums in
+    // sorted order and sets its head's keep bits.
+    {
       int P2 = 1;
-      while (P2 < m) P2 <<= 1;
-      float part = 0.f;
-      for (int j = tid; j <= iw; j += kXaThreads) {
-        float mj = 0.f;
+      while (P2 < jmax - 1) P2 <<= 1;
+      const int rpt = (KT / 4) / P2 >= 2 ? 2 : 1;  // rows whose keys fit one key tile
+      const int nr = 4 * rpt;                      // rows per sort batch
+      auto row_keys = [&](int rr) __attribute__((always_inline)) {
+        const int t = rr / rpt;
+        uint16_t* tile = t == 0 ? Kt0 : t == 1 ? Kt1 : t == 2 ? Kt2 : Kt3;
+        return reinterpret_cast<uint64_t*>(tile) + (rr % rpt) * P2;
+      };
+      uint32_t* const hmw = reinterpret_cast<uint32_t*>(hm2);  // hm2 as 32-bit words
+      for (int r0 = 0; r0 < kXaWaves; r0 += nr) {
+        const bool mine = wave >= r0 && wave < r0 + nr;  // wave-uniform
+        const int qd = wave / 4, gw = g0 + wave % 4;
+        const bool rv = mine && gw < a.G && bv[qd];
+        const int iw = ib[qd];
+        const int m = iw - 1;  // candidates: blocks 1 .. iw-1
+        const int hqw = kvh * a.G + min(gw, a.G - 1);
+        const uint32_t bit = 1u << gw;
+        float target = 0.f, forced = 0.f;
+        if (mine) {
+          uint64_t* keys = row_keys(wave - r0);
+          float part = 0.f, f0 = 0.f, fi = 0.f;
+          if (rv) {
+            const float* srow = a.lse + ((static_cast<int64_t>(b) * a.Hq + hqw) * xa_row_offset(a.nqb) +
+                                         xa_row_offset(iw)) * kXaGroupsPerBlock;
+            for (int j = lane; j <= iw; j += 64) {
+              float mj = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(srow + j * kXaGroupsPerBlock + 4 * q);
+              for (int q = 0; q < 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(srow + j * kXaGroupsPerBlock + 4 * q);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (16 * iw + 4 * q + e < ng) mj += __builtin_amdgcn_exp2f(v[e] - rlt[w][4 * q + e]);
+                for (int e = 0; e < 4; ++e)
+                  if (16 * iw + 4 * q + e < ng) mj += __builtin_amdgcn_exp2f(v[e] - rlt[wave][4 * q + e]);
+              }
+              part += mj;
+              if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb + j] = mj;
+              if (j == 0) f0 = mj;
+              if (j == iw) fi = mj;
+              if (j >= 1 && j < iw)
+                keys[j - 1] = (static_cast<uint64_t>(__float_as_uint(mj)) << 32) |
+                              static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(j));
+            }
+          }
+          // the rest of the row's P2 slots (all of them for an empty row) sort last
+          for (int p = (rv ? max(m, 0) : 0) + lane; p < P2; p += 64) keys[p] = 0ull;
+          target = a.tau * wave_sum(part);
+          f0 = wave_sum(f0);  // one lane holds each, the others 0
+          fi = wave_sum(fi);
+          forced = iw > 0 ? f0 + fi : f0;
         }
-        part += mj;
-        if (a.mass) a.mass[((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb + j] = mj;
-        if (j == 0) fz[0] = mj;
-        if (j == iw) fz[1] = mj;
-        if (j >= 1 && j < iw)
-          keys[j - 1] = (static_cast<uint64_t>(__float_as_uint(mj)) << 32) |
-                        static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(j));
-      }
-      for (int p = m + tid; p < P2; p += kXaThreads)
-        if (p >= 0) keys[p] = 0ull;
-      const float total = block_sum(part, redf);  // its barriers publish keys and fz
-      const float target = a.tau * total;
-      const float forced = iw > 0 ? fz[0] + fz[1] : fz[0];
-      if (m > 0) {
-        // bitonic sort, descending
+        __syncthreads();  // every row's keys written
+        // bitonic sort of each row's P2 keys, descending; stage (k, jj) pairs
+        // slot p (bit jj clear) with p + jj
         for (int k = 2; k <= P2; k <<= 1) {
           for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int p = tid; p < P2; p += kXaThreads) {
-              const int q = p ^ jj;
-              if (q > p) {
-                const uint64_t x0 = keys[p], x1 = keys[q];
-                const bool desc = (p & k) == 0;
-                if (desc ? (x0 < x1) : (x0 > x1)) {
-                  keys[p] = x1;
-                  keys[q] = x0;
-                }
+            for (int x = tid; x < nr * (P2 / 2); x += kXaThreads) {
+              const int rr = x / (P2 / 2), y = x % (P2 / 2);
+              const int p = ((y & ~(jj - 1)) << 1) | (y & (jj - 1)), q = p | jj;
+              uint64_t* keys = row_keys(rr);
+              const uint64_t x0 = keys[p], x1 = keys[q];
+              const bool desc = (p & k) == 0;
+              if (desc ? (x0 < x1) : (x0 > x1)) {
+                keys[p] = x1;
+                keys[q] = x0;
               }
             }
             __syncthreads();
           }
         }
-        // exclusive prefix of the sorted masses; keep entry p while the mass
-        // kept before it is still short of the target
-        const int per = (P2 + kXaThreads - 1) / kXaThreads;
-        const int p0 = tid * per;
-        float mine = 0.f;
-        for (int p = p0; p < min(p0 + per, m); ++p) mine += __uint_as_float(static_cast<uint32_t>(keys[p] >> 32));
-        float all;
-        float before = block_exclusive(mine, redf, &all);
-        for (int p = p0; p < min(p0 + per, m); ++p) {
-          const float v = __uint_as_float(static_cast<uint32_t>(keys[p] >> 32));
-          if (forced + before < target) {
-            const int j = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(keys[p]));
-            hm[j] |= bit;
+        if (rv && m > 0) {
+          // exclusive prefix of the sorted masses (each lane a run of slots);
+          // keep entry p while the mass kept before it is short of the target
+          const uint64_t* keys = row_keys(wave - r0);
+          const int per = (P2 + 63) / 64;
+          const int p0 = lane * per;
+          float mine_sum = 0.f;
+          for (int p = p0; p < min(p0 + per, m); ++p)
+            mine_sum += __uint_as_float(static_cast<uint32_t>(keys[p] >> 32));
+          float incl = mine_sum;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
           }
-          before += v;
+          float before = incl - mine_sum;
+          for (int p = p0; p < min(p0 + per, m); ++p) {
+            const float v = __uint_as_float(static_cast<uint32_t>(keys[p] >> 32));
+            if (forced + before < target) {
+              const int j = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(keys[p]));
+              atomicOr(&hmw[(qd * a.nqb + j) >> 1], bit << (16 * ((qd * a.nqb + j) & 1)));
+            }
+            before += v;
+          }
+        }
+        if (rv && lane == 0) {
+          atomicOr(&hmw[(qd * a.nqb) >> 1], bit << (16 * ((qd * a.nqb) & 1)));
+          atomicOr(&hmw[(qd * a.nqb + iw) >> 1], bit << (16 * ((qd * a.nqb + iw) & 1)));
+        }
+        __syncthreads();  // keep bits set; the key tiles are free for the next batch
+        if (rv && a.keep) {
+          const uint16_t* hm = hm2 + qd * a.nqb;
+          uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb;
+          for (int j = lane; j <= iw; j += 64) krow[j] = (hm[j] & bit) ? 1 : 0;
         }
       }
-      if (tid == 0) {
-        hm[0] |= bit;
-        hm[iw] |= bit;
-      }
-      __syncthreads();
-      if (a.keep) {
-        uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb;
-        for (int j = tid; j <= iw; j += kXaThreads) krow[j] = (hm[j] & bit) ? 1 : 0;
-      }
     }
-    __syncthreads();  // the sort buffer (first key tile) is free again
+    __syncthreads();  // the key tiles are free again
   }
 
   // Ascending list of the key blocks some head of the group keeps, for each
