@@ -209,6 +209,39 @@ def test_xa_full_size_sampled():
     assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(lse).all())
 
 
+def test_xa_long_rows_sort_in_half_batches():
+    """A sequence of more than 1,025 XA blocks at d = 64: each row then has
+    2,048 sort slots, two rows no longer fit one key tile, and the selection
+    sorts its rows four at a time.  Masses and keep rows of sampled query
+    blocks against the oracle, and the keep flags of every row are a valid
+    selection: blocks 0 and i kept, nothing past i."""
+    L = 1100 * 128 + 45
+    c = gen.custom_case(131, [L], 8, 2, 64, "bf16", n_sink=1, keep_fraction=0.2,
+                        hitters=(0.1, 8.0))
+    modes = np.array([[1, 1]], np.int8)  # FA-XA: both KV heads in XA mode
+    cmodes = xa.computation_modes(modes, "FA-XA")
+    note(f"xa long rows d=64 L={L}")
+    O, lse, mass, keep = run_xa(c, modes, "FA-XA", 0.9)
+    nb = -(-L // 128)
+    rows = [0, 2, 700, 1026, nb - 1]
+    scale = 1.0 / np.sqrt(c.d)
+    for hq in (0, 5):
+        A = xa.block_mass_rows(Bf16View(c.q)[:, hq], Bf16View(c.k)[:, hq // 4], rows, scale=scale)
+        for ri, i in enumerate(rows):
+            err = np.abs(mass[0, hq, i, :i + 1] - A[ri, :i + 1]).max()
+            assert err <= MASS_TOL, f"mass hq={hq} i={i}: {err:.2e}"
+            want = xa.select_row(A[ri], i, 0.9)
+            gk = keep[0, hq, i, :i + 1].astype(bool)
+            if not (gk == want).all():
+                assert not robust(A[ri], i, 0.9), f"keep row hq={hq} i={i} differs away from a tie"
+    k = keep[0]
+    assert (k[:, np.arange(nb), 0] == 1).all() and (k[:, np.arange(nb), np.arange(nb)] == 1).all()
+    iu, ju = np.triu_indices(nb, 1)
+    il, jl = np.tril_indices(nb)
+    assert (k[:, iu, ju] == 7).all() and np.isin(k[:, il, jl], (0, 1)).all()
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(lse).all())
+
+
 def test_xa_plan_and_run_equal_the_one_shot_call():
     c = gen.custom_case(91, [2500, 900], 8, 2, 128, "bf16", n_sink=1, keep_fraction=0.2,
                         hitters=(0.1, 8.0))
