@@ -196,7 +196,20 @@ __global__ __launch_bounds__(kSortWaves * 64) void key_sort_kernel(const uint32_
   __syncthreads();
   const int64_t per = (n + kSortWaves - 1) / kSortWaves;
   const int64_t seg0 = min(n, per * wave), seg1 = min(n, seg0 + per);
-  for (int64_t i = seg0 + lane; i < seg1; i += 64) atomicAdd(&hist[wave][min(keys[i], kSortBands - 1u)], 1);
+  // (a step whose 64 keys are all equal, the common case in a band-sorted
+  // list, adds its count with one atomic instead of 64 to the same word)
+  for (int64_t base = seg0; base < seg1; base += 64) {
+    const int64_t i = base + lane;
+    const bool valid = i < seg1;
+    const uint32_t k = valid ? min(keys[i], kSortBands - 1u) : 0xFFFFFFFFu;
+    const uint32_t k0 = __builtin_amdgcn_readfirstlane(k);
+    const uint64_t nval = __ballot(valid);
+    if (__ballot(valid && k == k0) == nval) {
+      if (lane == 0) atomicAdd(&hist[wave][k0], static_cast<int32_t>(__popcll(nval)));
+    } else if (valid) {
+      atomicAdd(&hist[wave][k], 1);
+    }
+  }
   __syncthreads();
   // thread t owns key t (kSortBands == kSortWaves * 64): its total over the
   // waves, scanned across keys, then split back over the waves
@@ -233,10 +246,16 @@ __global__ __launch_bounds__(kSortWaves * 64) void key_sort_kernel(const uint32_
     const int64_t i = base + lane;
     const bool valid = i < seg1;
     const uint32_t k = valid ? min(keys[i], kSortBands - 1u) : 0xFFFFFFFFu;
-    uint64_t same = 0;
-    for (int j = 0; j < 64; ++j) {
-      const uint32_t kj = __builtin_amdgcn_readlane(k, j);
-      same |= static_cast<uint64_t>(kj == k) << j;
+    // lanes holding this lane's key: one ballot when the whole step shares
+    // one key, else a pass over the lanes
+    const uint32_t k0 = __builtin_amdgcn_readfirstlane(k);
+    uint64_t same = __ballot(k == k0);
+    if (same != ~uint64_t(0)) {
+      same = 0;
+      for (int j = 0; j < 64; ++j) {
+        const uint32_t kj = __builtin_amdgcn_readlane(k, j);
+        same |= static_cast<uint64_t>(kj == k) << j;
+      }
     }
     const uint64_t below = (uint64_t(1) << lane) - 1;
     const int rank = __popcll(same & below);
