@@ -187,9 +187,15 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
   __shared__ float rlt[kXaWaves][kXaGroupsPerBlock];  // group-row totals of the waves' (head, block)
   __shared__ int32_t redi[kXaWaves + 1];
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // [2][nqb]: heads keeping key block j, for the pair's upper and lower block
-  // (a group has at most 16 query heads)
-  uint16_t* hm2 = reinterpret_cast<uint16_t*>(smem);
+  // [2][nqb] 16-bit masks of the heads keeping key block j, for the pair's
+  // upper and lower block (a group has at most 16 query heads), two to a
+  // 32-bit word so that the waves of different heads set bits by LDS atomics
+  uint32_t* hmw = reinterpret_cast<uint32_t*>(smem);
+  // keep mask of the pair's block qd (0 upper, 1 lower) at key block j
+  auto hm_at = [&](int qd, int j) __attribute__((always_inline)) {
+    const int x = qd * a.nqb + j;
+    return (hmw[x >> 1] >> (16 * (x & 1))) & 0xFFFFu;
+  };
 
   // Work item t = the workgroup's position in the XCD-chunked order
   // (list_position): a pair of query blocks (2 p + 1, 2 p) of one XA row;
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
   const int i = ib[quad];         // this wave's query block
   const bool iv = bv[quad];
   const int r = lane % 16, kq = lane / 16;
-  for (int j = tid; j < 2 * a.nqb; j += kXaThreads) hm2[j] = 0;
+  for (int j = tid; j < a.nqb; j += kXaThreads) hmw[j] = 0u;  // 2 nqb 16-bit masks
 
   // Direct loads of key block j: instruction q = wave NDMA + n of the tile
   // fills rows (q % IPG) RPI .. + RPI - 1 of group q / IPG, lane l writing
@@ -402,7 +408,6 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
         uint16_t* tile = t == 0 ? Kt0 : t == 1 ? Kt1 : t == 2 ? Kt2 : Kt3;
         return reinterpret_cast<uint64_t*>(tile) + (rr % rpt) * P2;
       };
-      uint32_t* const hmw = reinterpret_cast<uint32_t*>(hm2);  // hm2 as 32-bit words
       for (int r0 = 0; r0 < kXaWaves; r0 += nr) {
         const bool mine = wave >= r0 && wave < r0 + nr;  // wave-uniform
         const int qd = wave / 4, gw = g0 + wave % 4;
@@ -493,9 +498,8 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
         }
         __syncthreads();  // keep bits set; the key tiles are free for the next batch
         if (rv && a.keep) {
-          const uint16_t* hm = hm2 + qd * a.nqb;
           uint8_t* krow = a.keep + ((static_cast<int64_t>(b) * a.Hq + hqw) * a.nqb + iw) * a.nqb;
-          for (int j = lane; j <= iw; j += 64) krow[j] = (hm[j] & bit) ? 1 : 0;
+          for (int j = lane; j <= iw; j += 64) krow[j] = (hm_at(qd, j) & bit) ? 1 : 0;
         }
       }
     }
@@ -507,16 +511,16 @@ __global__ __launch_bounds__(kXaThreads) void xa_plan_kernel(XaArgs a) {
   for (int qd = 0; qd < 2; ++qd) {
     if (!bv[qd]) continue;  // workgroup-uniform
     const int iw = ib[qd];
-    const uint16_t* hm = hm2 + qd * a.nqb;
     const int per = (iw + 1 + kXaThreads - 1) / kXaThreads;
     const int j0 = tid * per;
     int32_t mine = 0;
-    for (int j = j0; j < min(j0 + per, iw + 1); ++j) mine += hm[j] != 0;
+    for (int j = j0; j < min(j0 + per, iw + 1); ++j) mine += hm_at(qd, j) != 0u;
     int32_t count;
     int32_t pos = block_exclusive(mine, redi, &count);
     int32_t* lrow = a.list + static_cast<int64_t>(bk) * xa_row_offset(a.nqb) + xa_row_offset(iw);
     for (int j = j0; j < min(j0 + per, iw + 1); ++j) {
-      if (hm[j] != 0) lrow[pos++] = j | (static_cast<int32_t>(hm[j]) << 16);
+      const uint32_t h = hm_at(qd, j);
+      if (h != 0u) lrow[pos++] = j | static_cast<int32_t>(h << 16);
     }
     if (tid == 0) a.cnt[static_cast<int64_t>(bk) * a.nqb + iw] = count;
     __syncthreads();  // redi is reused by the next block's prefix
