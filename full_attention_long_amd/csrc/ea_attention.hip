@@ -363,12 +363,17 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
   // XA item: the ascending list of the tile's XA query block (entries
   // j | head mask << 16 for kept 128-blocks j, each two 64-blocks), less the
   // diagonal block's second half when the tile ends before it
-  const int32_t* xl = nullptr;
+  // (read through the constant address space: the list does not change
+  // during the launch, so its entries come by scalar loads, which the DMA
+  // loads' vmcnt does not count; as ordinary global loads, every entry read
+  // waited for all the tile loads in flight)
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  cint32* xl = nullptr;
   if constexpr (XA) {
     if (mode == kModeXA) {
       const int xi = p0 / kXaBlock;
       const int64_t bk = static_cast<int64_t>(b) * a.Hkv + kvh;
-      xl = a.xa_list + bk * xa_row_offset(a.xa_nqb) + xa_row_offset(xi);
+      xl = (cint32*)(a.xa_list + bk * xa_row_offset(a.xa_nqb) + xa_row_offset(xi));
       nblk = 2 * a.xa_cnt[bk * a.xa_nqb + xi] - (2 * xi + 1 > qb1 ? 1 : 0);
     }
   }
