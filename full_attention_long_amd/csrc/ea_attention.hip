@@ -377,9 +377,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
       nblk = 2 * a.xa_cnt[bk * a.xa_nqb + xi] - (2 * xi + 1 > qb1 ? 1 : 0);
     }
   }
+  // The entries m = n / 2 and m + 1 that the pair of blocks n, n + 1 and
+  // their loads ahead need stay in registers, and the next one is loaded a
+  // pair ahead (read where it is needed, each entry's scalar load was waited
+  // for at once, after the barrier, before any matrix work of the block).
+  int xm = 0, xe0 = 0, xe1 = 0, xlast = 0;
+  if constexpr (XA) {
+    if (mode == kModeXA && nblk > 0) {
+      xlast = (nblk + 1) / 2 - 1;
+      xe0 = xl[0];
+      xe1 = xl[min(1, xlast)];
+    }
+  }
+  // (for n in [2 xm, 2 xm + 3], the range every caller stays in)
   auto kb_of = [&](int n) {
     if constexpr (XA) {
-      if (mode == kModeXA) return 2 * (xl[n >> 1] & 0xFFFF) + (n & 1);
+      if (mode == kModeXA) return 2 * (((n >> 1) == xm ? xe0 : xe1) & 0xFFFF) + (n & 1);
     }
     return n < r1_end ? n : r2_beg + (n - r1_end);
   };
@@ -586,7 +599,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     bool full;
     if constexpr (XA) {
       if (mode == kModeXA) {
-        hmask = static_cast<uint32_t>(xl[n >> 1]) >> 16;
+        hmask = static_cast<uint32_t>(xe0) >> 16;  // entry n / 2 = xm
         full = hmask == (1u << a.G) - 1u && kb * kBlock + kBlock - 1 <= p0;
       } else {
         full = block_full(mode, kb, p0, qb0, qb1, ns, w);
@@ -608,8 +621,17 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attention_kernel_bf16(Attn
     __syncthreads();
   };
   for (int n = 0; n < nblk; n += 2) {
+    int xe2 = 0;
+    if constexpr (XA) {
+      if (mode == kModeXA) xe2 = xl[min(xm + 2, xlast)];
+    }
     iter(n, sa0, sa1, sb0, sb1, Ks0, Ks1, Vs1, Vs0);
     if (n + 1 < nblk) iter(n + 1, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs1);
+    if constexpr (XA) {
+      ++xm;
+      xe0 = xe1;
+      xe1 = xe2;
+    }
   }
   }
 
